@@ -1,0 +1,263 @@
+"""Benchmark of the TP1 decode projection on one MI355X.
+
+Default run: the o_proj sweep workload (W 7168 x 12288 BF16, x[B, 12288],
+B = 1, 2, 4, 8, 16, seed 1).  One step = one projection call per batch size,
+each on its own weight copy from a rotation of distinct copies (>= 1 GB in
+total, so no call finds its weight in the 256 MB MALL).  Inputs are resident
+in HBM before timing starts.  Prints ONE JSON line:
+  value        = algorithmic HBM bytes of a step / step time, GB/s
+  roofline     = the dominant kernel's achieved GB/s against the 8 TB/s peak
+  cpu_baseline = the CPU oracle timed on a bounded sample of the same step
+
+`--report PATH` also times every point of every configuration (DSA B=1, the
+o_proj, KDA and DSA sweeps, the 8-layer stream), the plain streaming-read
+ceiling and the cache-assisted ("hot", one weight repeated) figures, and
+writes them as JSON to PATH.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HEADLINE = "oproj_sweep"
+
+
+def _args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--report", default=None, help="write the all-config report here")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    return ap.parse_args()
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def headline(args, torch, tp, wl, timing):
+    cfg = wl.BY_NAME[HEADLINE]
+    t = wl.config_tensors(cfg)
+    dev = torch.device("cuda:0")
+    W0 = t["W"].to(dev)
+    x = t["x"].to(dev)
+    copies = timing.rotation_copies(W0)
+    plan = tp.Plan(cfg.N, cfg.K, cfg.batches)
+    outs = {B: torch.empty((B, cfg.N), dtype=torch.bfloat16, device=dev) for B in cfg.batches}
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    xs = {B: x[:B] for B in cfg.batches}
+    nb = len(cfg.batches)
+    ncopy = len(copies)
+
+    def call(i, B):
+        W = copies[i % ncopy]
+        rc = plan.run_ptr(B, xs[B].data_ptr(), cfg.K, W.data_ptr(), outs[B].data_ptr(), sh)
+        if rc != 0:
+            raise tp.ProjError(rc, f"proj_run B={B}")
+
+    def step(s):
+        for j, B in enumerate(cfg.batches):
+            call(s * nb + j, B)
+
+    for s in range(args.warmup):
+        step(s)
+    # per-call HIP events on the launch stream, over the timed region
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in cfg.batches] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        for j, B in enumerate(cfg.batches):
+            ev[s][j][0].record(stream)
+            call(s * nb + j, B)
+            ev[s][j][1].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    step_bytes = sum(wl.algorithmic_bytes(B, cfg.N, cfg.K) for B in cfg.batches)
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    per_b = {}
+    for j, B in enumerate(cfg.batches):
+        us = [ev[s][j][0].elapsed_time(ev[s][j][1]) * 1e3 for s in range(args.steps)]
+        mean = sum(us) / len(us)
+        tac, _ = plan.tactic(B)
+        per_b[B] = {"us_per_call": round(mean, 2),
+                    "GBps": round(timing.gbs(wl.algorithmic_bytes(B, cfg.N, cfg.K), mean), 1),
+                    "kernel": plan.kernel_name(B), "tactic": tac.as_dict()}
+    # dominant kernel: the one with the largest share of the step's GPU time
+    by_kernel = {}
+    for B, r in per_b.items():
+        k = by_kernel.setdefault(r["kernel"], {"us": 0.0, "bytes": 0, "calls": 0})
+        k["us"] += r["us_per_call"]
+        k["bytes"] += wl.algorithmic_bytes(B, cfg.N, cfg.K)
+        k["calls"] += 1
+    name, k = max(by_kernel.items(), key=lambda kv: kv[1]["us"])
+    avg_us = k["us"] / k["calls"]
+    bytes_per_launch = k["bytes"] / k["calls"]
+    achieved = timing.gbs(bytes_per_launch, avg_us)
+    roof = {"bound": "hbm", "kernel": name, "achieved": round(achieved, 1),
+            "peak": timing.HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / timing.HBM_PEAK_GBS, 4), "traffic": None,
+            "avg_launch_us": round(avg_us, 2), "bytes_per_launch": int(bytes_per_launch)}
+    res = {"cfg": cfg, "t": t, "plan": plan, "value": value, "ms": ms_per_step,
+           "per_b": per_b, "roofline": roof, "step_bytes": step_bytes,
+           "copies": ncopy}
+    return res
+
+
+def cpu_baseline(args, cfg, t, wl):
+    import oracle
+    xb = wl.bits(t["x"])
+    wb = wl.bits(t["W"])
+    threads = oracle.default_threads()
+    oracle.proj(xb[:1], wb[:64], threads=threads)       # load / warm the library
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        for B in cfg.batches:
+            oracle.proj(xb[:B], wb, threads=threads)
+        reps += 1
+        if time.perf_counter() - t0 >= args.cpu_seconds or reps >= 50:
+            break
+    el = time.perf_counter() - t0
+    step_bytes = sum(wl.algorithmic_bytes(B, cfg.N, cfg.K) for B in cfg.batches)
+    return {"value": round(step_bytes * reps / el / 1e9, 3), "unit": "GB/s",
+            "cores": threads, "kind": "oracle",
+            "sample": f"{reps} full steps of the o_proj sweep (B=1,2,4,8,16 on one "
+                      f"7168x12288 weight), {el:.1f} s, FP64 accumulation",
+            "ms_per_step": round(el * 1e3 / reps, 1)}
+
+
+def report(args, torch, tp, wl, timing):
+    """Every configuration point, cold (rotated weights) and hot."""
+    dev = torch.device("cuda:0")
+    out = {"points": [], "device": torch.cuda.get_device_name(0)}
+    # plain streaming-read ceiling over a 2 GB buffer
+    buf = torch.empty(2 * 1024 ** 3 // 2, dtype=torch.bfloat16, device=dev)
+    buf.fill_(1.0)
+    sink = torch.empty(65536, dtype=torch.float32, device=dev)
+    probe = {}
+    for wpc in (4, 8, 16, 32):
+        r = timing.time_calls([lambda: tp.read_probe(buf, sink, wpc)], warmup=3, reps=20)
+        probe[wpc] = round(timing.gbs(buf.numel() * 2, r["us_median"]), 1)
+    out["read_ceiling_GBps"] = probe
+    _say(f"read ceiling (GB/s by waves/CU): {probe}")
+    del buf
+    for cfg in wl.CONFIGS:
+        if cfg.layers > 1:
+            continue
+        t = wl.config_tensors(cfg)
+        W0 = t["W"].to(dev)
+        x = t["x"].to(dev)
+        copies = timing.rotation_copies(W0)
+        plan = tp.Plan(cfg.N, cfg.K, cfg.batches)
+        for B in cfg.batches:
+            y = torch.empty((B, cfg.N), dtype=torch.bfloat16, device=dev)
+            xb = x[:B]
+            calls = [(lambda W=W: plan.run(xb, W, y)) for W in copies]
+            cold = timing.time_calls(calls, warmup=3, reps=60)
+            hot = timing.time_calls([lambda: plan.run(xb, W0, y)], warmup=3, reps=30)
+            nbytes = wl.algorithmic_bytes(B, cfg.N, cfg.K)
+            tac, _ = plan.tactic(B)
+            p = {"config": cfg.name, "N": cfg.N, "K": cfg.K, "B": B,
+                 "us_median": round(cold["us_median"], 2), "us_p10": round(cold["us_p10"], 2),
+                 "us_p90": round(cold["us_p90"], 2), "us_b2b": round(cold["us_mean_b2b"], 2),
+                 "GBps": round(timing.gbs(nbytes, cold["us_median"]), 1),
+                 "pct_peak": round(100 * timing.gbs(nbytes, cold["us_median"]) / timing.HBM_PEAK_GBS, 1),
+                 "hot_us": round(hot["us_median"], 2),
+                 "TFLOPs": round(2.0 * B * cfg.N * cfg.K / (cold["us_median"] * 1e-6) / 1e12, 1),
+                 "kernel": plan.kernel_name(B), "tactic": tac.as_dict()}
+            out["points"].append(p)
+            _say(f"{cfg.name:12s} B={B:3d} {p['us_median']:8.2f} us {p['GBps']:8.1f} GB/s "
+                 f"{p['pct_peak']:5.1f}% hot {p['hot_us']:7.2f} us  {p['kernel']}")
+        del copies, W0, x, t
+        torch.cuda.empty_cache()
+    # multi-layer stream: 8 x (in-proj 14560x7168 -> o_proj 7168x12288), B = 64
+    cfg = wl.BY_NAME["multilayer"]
+    g = torch.Generator(device=dev)
+    g.manual_seed(cfg.seed)
+    w_in = [(torch.randn((wl.DSA_N, wl.DSA_K), generator=g, device=dev) * 0.02).to(torch.bfloat16)
+            for _ in range(cfg.layers)]
+    w_o = [(torch.randn((wl.OPROJ_N, wl.OPROJ_K), generator=g, device=dev) * 0.02).to(torch.bfloat16)
+           for _ in range(cfg.layers)]
+    x0 = torch.randn((cfg.bmax, wl.DSA_K), generator=g, device=dev).to(torch.bfloat16)
+    pin = tp.Plan(wl.DSA_N, wl.DSA_K, [cfg.bmax])
+    po = tp.Plan(wl.OPROJ_N, wl.OPROJ_K, [cfg.bmax])
+    stack = tp.LayerStack(pin, po, w_in, w_o)
+    y_in, y_o = stack.buffers(cfg.bmax)
+    r = timing.time_calls([lambda: stack.run(x0, y_in, y_o)], warmup=3, reps=20)
+    nbytes = cfg.layers * (wl.algorithmic_bytes(cfg.bmax, wl.DSA_N, wl.DSA_K)
+                           + wl.algorithmic_bytes(cfg.bmax, wl.OPROJ_N, wl.OPROJ_K))
+    out["multilayer"] = {"layers": cfg.layers, "B": cfg.bmax, "us_median": round(r["us_median"], 1),
+                         "GBps": round(timing.gbs(nbytes, r["us_median"]), 1),
+                         "bytes": nbytes, "in_kernel": pin.kernel_name(cfg.bmax),
+                         "o_kernel": po.kernel_name(cfg.bmax)}
+    _say(f"multilayer 8x(in+o) B=64: {out['multilayer']}")
+    with open(args.report, "w") as f:
+        json.dump(out, f, indent=1)
+    return out
+
+
+def main():
+    args = _args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU only: the projection "
+                          "runs on one GPU's share (one DEP rank) and nothing here "
+                          "shards or communicates; run with --gpus 1"}))
+        sys.exit(2)
+    import torch
+
+    import tp1_skinny_bf16_amd as tp
+    import workloads as wl
+    from tp1_skinny_bf16_amd import timing
+
+    if not torch.cuda.is_available():
+        print(json.dumps({"error": "no GPU visible"}))
+        sys.exit(1)
+    torch.cuda.set_device(0)
+    h = headline(args, torch, tp, wl, timing)
+    cpu = None
+    if not args.no_cpu:
+        cpu = cpu_baseline(args, h["cfg"], h["t"], wl)
+    if args.report:
+        report(args, torch, tp, wl, timing)
+    cfg = h["cfg"]
+    line = {
+        "metric": "achieved HBM GB/s (algorithmic W+x+y bytes / time), TP1 BF16 decode "
+                  "projection, o_proj sweep",
+        "value": round(h["value"], 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(h["ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "o_proj sweep: W 7168x12288 BF16 ~N(0,0.02), x[B,12288] ~N(0,1), "
+                               "B in {1,2,4,8,16}, seed 1; one call per B per step",
+                   "N": cfg.N, "K": cfg.K, "batches": list(cfg.batches),
+                   "weight_copies": h["copies"], "step_bytes": h["step_bytes"]},
+        "per_batch_us": {str(B): r["us_per_call"] for B, r in h["per_b"].items()},
+        "per_batch_GBps": {str(B): r["GBps"] for B, r in h["per_b"].items()},
+        "kernels": {str(B): r["kernel"] for B, r in h["per_b"].items()},
+        "roofline": h["roofline"],
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,195 @@
+/*
+ * tp1_proj.h -- C ABI of the TP1 decode projection on MI355X (gfx950).
+ *
+ * The operation is the TP1 linear of the vLLM API page
+ * "vllm.models.kimi_k3.nvidia.specialized_decode.runtime.dep", section
+ * "DepProjection":
+ *
+ *     y[B, N] = x[B, K] . W^T          (W is N x K, row-major: nn.Linear)
+ *
+ * with BF16 x, W and y and FP32 accumulation (the page's opening text: the
+ * stock layer's precision, FP32 accumulation and BF16 outputs, the split-K
+ * summation order free).  Outputs are rounded once from the FP32 sum to the
+ * nearest BF16, ties to even.
+ *
+ * A plan is built once per weight shape for a list of batch sizes (the
+ * page's DepProjection binds a weight to a per-batch tactic table; section
+ * "_bins" gives the lookup rule, section "dep_policies" the table per batch).
+ * Unlike the page, the weight is passed to every run, so one plan serves
+ * every layer of the same shape, and there is no second backend: every
+ * planned batch runs a hand-written kernel of this library.
+ *
+ * All pointers to x, W and y are device pointers on the device that was
+ * current when the plan was built.  All calls are host calls; proj_run only
+ * enqueues work on the given stream and never synchronises.
+ */
+#ifndef TP1_PROJ_H
+#define TP1_PROJ_H
+
+#include <stddef.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes.  Every entry point returns one of these (0 = success). */
+enum proj_status {
+    PROJ_OK = 0,
+    PROJ_EINVAL = -1,  /* bad argument: NULL pointer, N/K <= 0, K % 8 != 0,
+                          empty / unsorted / out-of-range batch list, ...   */
+    PROJ_EBATCH = -2,  /* run with B < 0 or B > the largest planned batch  */
+    PROJ_EALIGN = -3,  /* x, W or y not 16-byte aligned, or ldx % 8 != 0   */
+    PROJ_EHIP = -4,    /* a HIP runtime call failed (no device, launch...) */
+    PROJ_ENOMEM = -5,  /* host or device allocation failed                 */
+    PROJ_ENODEV = -6   /* the plan was built host-only and cannot run      */
+};
+
+/* Kernel families a tactic can name. */
+enum proj_kernel {
+    PROJ_KERNEL_STREAM = 1, /* split-K weight stream: VALU dot products,
+                               lanes along K, wavefront reductions         */
+    PROJ_KERNEL_MFMA = 2    /* BF16 MFMA tiles (16x16x32), FP32 accumulate */
+};
+
+/* Plan flags. */
+#define PROJ_PLAN_HOST_ONLY 0x1u /* build and validate the tactic table
+                                    without touching a device: the plan can
+                                    be queried but proj_run returns
+                                    PROJ_ENODEV                             */
+
+/* Limits checked by proj_plan. */
+#define PROJ_MAX_BATCH 256       /* largest batch a plan may list          */
+#define PROJ_MAX_BATCHES 64      /* longest batch list                     */
+
+/*
+ * A tactic: how one batch bin runs.  Filled in from the library's measured
+ * table (or its default rule for shapes it has not measured), or set with
+ * proj_plan_set_tactic.
+ *   kernel : enum proj_kernel
+ *   bcap   : batch capacity of the kernel instance (>= the bin)
+ *   split  : number of K slices S; S > 1 adds a fixed-order reduction pass
+ *   rows   : STREAM: W rows a wave carries per pass (1, 2 or 4)
+ *            MFMA:   16-column N tiles per wave (1, 2 or 4; 1 at bcap 256)
+ *   waves  : waves per workgroup (STREAM 1..8, MFMA 1..4)
+ *   wpc    : STREAM: waves per compute unit the grid is sized for
+ *            MFMA:   0 = one wave per N range (grid from N), else as STREAM
+ */
+typedef struct proj_tactic {
+    int kernel;
+    int bcap;
+    int split;
+    int rows;
+    int waves;
+    int wpc;
+} proj_tactic_t;
+
+typedef struct proj_plan_s proj_plan_t;
+
+/*
+ * proj_plan -- build a plan for an N x K weight and a list of batch sizes.
+ *   N, K      : weight rows / columns; N > 0, K > 0, K % 8 == 0
+ *   batches   : strictly increasing, 1 <= b <= PROJ_MAX_BATCH, length
+ *               1..PROJ_MAX_BATCHES (host array, not retained)
+ *   flags     : 0 or PROJ_PLAN_HOST_ONLY
+ *   out       : receives the plan (set to NULL on failure)
+ * The plan owns an FP32 split-K workspace allocated with hipMalloc on the
+ * current device (none for host-only plans); proj_free releases it.
+ * Returns PROJ_OK, PROJ_EINVAL, PROJ_ENOMEM or PROJ_EHIP.
+ */
+int proj_plan(int N, int K, const int *batches, int n_batches, unsigned flags,
+              proj_plan_t **out);
+
+/*
+ * proj_run -- enqueue y[0:B] = x[0:B] . W^T on `stream`.
+ *   B      : 0 <= B <= max(batches); B == 0 is a no-op.  1 <= B runs the
+ *            tactic of the smallest planned batch >= B (the "_bins" rule).
+ *   x      : BF16 [B, K] device pointer, row stride ldx elements
+ *            (ldx == 0 means K; ldx >= K, ldx % 8 == 0), 16-byte aligned
+ *   W      : BF16 [N, K] device pointer, contiguous rows, 16-byte aligned
+ *   y      : BF16 [B, N] device pointer, contiguous (row stride N),
+ *            16-byte aligned; must not overlap x or W
+ *   stream : a hipStream_t (NULL = the default stream)
+ * One plan supports one stream at a time: runs on different streams that
+ * overlap in time share the plan's workspace and race.
+ * Returns PROJ_OK, PROJ_EINVAL, PROJ_EBATCH, PROJ_EALIGN, PROJ_ENODEV or
+ * PROJ_EHIP (launch failure; faults inside a kernel surface at the
+ * caller's next synchronisation).
+ */
+int proj_run(const proj_plan_t *plan, int B, const void *x, long ldx,
+             const void *W, void *y, void *stream);
+
+/*
+ * proj_run_layers -- multi-layer decode streaming: enqueue, for l = 0..L-1,
+ *     y_in[l] = x_l . W_in[l]^T                    (plan `in`,  N_in x K_in)
+ *     y_o[l]  = y_in[l][:, 0:K_o] . W_o[l]^T       (plan `out`, N_o x K_o)
+ *     x_{l+1} = y_o[l]
+ * back to back on one stream, each layer with its own weights, as the
+ * dep page's DepAttention chains its input projection into o_proj (section
+ * "DepAttention"; here the attention core between them is replaced by a
+ * fixed gather of the first K_o columns, read in place through the row
+ * stride N_in, without a copy).
+ *   in, out : plans with out.N == in.K and out.K <= in.N; B must be within
+ *             both plans' batch ranges
+ *   x0      : BF16 [B, K_in], row stride ldx0 (0 = K_in)
+ *   W_in    : host array of L device pointers to BF16 [N_in, K_in]
+ *   W_o     : host array of L device pointers to BF16 [N_o, K_o]
+ *   y_in    : BF16 [L, B, N_in] device buffer (every layer's input projection)
+ *   y_o     : BF16 [L, B, N_o] device buffer (every layer's output)
+ * Returns as proj_run; on an error no later layer is enqueued.
+ */
+int proj_run_layers(const proj_plan_t *in, const proj_plan_t *out, int L, int B,
+                    const void *x0, long ldx0, const void *const *W_in,
+                    const void *const *W_o, void *y_in, void *y_o, void *stream);
+
+/* proj_free -- release a plan and its workspace.  NULL is a no-op. */
+void proj_free(proj_plan_t *plan);
+
+/* proj_strerror -- static text for a status code. */
+const char *proj_strerror(int code);
+
+/*
+ * proj_plan_tactic -- the tactic proj_run would use for batch B, and the
+ * planned bin it falls in (bin may be NULL).  Returns PROJ_EBATCH when B is
+ * outside 1..max(batches).
+ */
+int proj_plan_tactic(const proj_plan_t *plan, int B, proj_tactic_t *tactic,
+                     int *bin);
+
+/*
+ * proj_plan_set_tactic -- replace the tactic of planned bin `bin` (used to
+ * measure candidates).  The tactic is validated against the plan's shape
+ * (PROJ_EINVAL when no kernel instance or LDS budget fits it).  When it
+ * needs more split-K workspace than the plan holds, the workspace is
+ * reallocated (hipFree + hipMalloc, which synchronise the device), so do not
+ * call it while runs of this plan are in flight.
+ */
+int proj_plan_set_tactic(proj_plan_t *plan, int bin,
+                         const proj_tactic_t *tactic);
+
+/*
+ * proj_plan_kernel_name -- the kernel instance(s) proj_run launches for
+ * batch B, as they appear in a profiler's kernel trace, e.g.
+ * "stream_kernel<1, 1, 16>" or "mfma_kernel<1, 2, 6>+splitk_reduce".
+ * Writes a NUL-terminated string of at most len bytes into buf.
+ */
+int proj_plan_kernel_name(const proj_plan_t *plan, int B, char *buf, size_t len);
+
+/* proj_plan_workspace_bytes -- bytes of device workspace the plan holds. */
+size_t proj_plan_workspace_bytes(const proj_plan_t *plan);
+
+/*
+ * proj_read_probe -- measurement aid, not part of the projection: enqueue a
+ * kernel that reads `bytes` (a multiple of 16) from device buffer `buf` with
+ * 128-bit loads and writes one float per workgroup into `sink` (device,
+ * at least 65536 floats), so the box's plain streaming-read ceiling can be
+ * timed with the same loads the projection uses.  `waves_per_cu` sizes the
+ * grid (0 = 8).
+ */
+int proj_read_probe(const void *buf, size_t bytes, float *sink,
+                    int waves_per_cu, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TP1_PROJ_H */

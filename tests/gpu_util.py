@@ -1,0 +1,105 @@
+"""Helpers of the GPU parity tests: run the HIP path through the C ABI and
+compare with the CPU oracle on the same seeded inputs."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+import parity
+import tp1_skinny_bf16_amd as tp
+import workloads as wl
+
+DEV = torch.device("cuda:0")
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def gpu_run(plan, x_cpu, W_dev, B=None, ldx_pad=0):
+    """y bits [B, N] of the HIP path; x optionally read with a row stride."""
+    B = x_cpu.shape[0] if B is None else B
+    K = x_cpu.shape[1]
+    if ldx_pad:
+        big = torch.zeros((B, K + ldx_pad), dtype=torch.bfloat16)
+        big[:, :K] = x_cpu[:B]
+        xd = big.to(DEV)[:, :K]
+    else:
+        xd = x_cpu[:B].contiguous().to(DEV)
+    y = torch.empty((B, plan.N), dtype=torch.bfloat16, device=DEV)
+    plan.run(xd, W_dev, y)
+    torch.cuda.synchronize()
+    return wl.bits(y.cpu())
+
+
+def sample_rows(N: int, B: int, K: int, budget: float = 4e9, seed: int = 0):
+    """Weight rows (output columns) the oracle checks: all when affordable,
+    else a seeded sample that always keeps the first and last 64 rows."""
+    if float(N) * B * K <= budget:
+        return np.arange(N)
+    m = max(256, int(budget / (B * K)))
+    rng = np.random.default_rng(seed)
+    mid = rng.choice(np.arange(64, N - 64), size=min(m, N - 128), replace=False)
+    return np.unique(np.concatenate([np.arange(64), np.arange(N - 64, N), mid]))
+
+
+def check_random(label, y_bits, x_cpu, W_cpu, cols=None, threads=None):
+    """G1/G2/D1 gates of y_bits against the oracle on columns `cols`."""
+    xb = wl.bits(x_cpu)
+    wb = wl.bits(W_cpu)
+    if cols is not None:
+        wsub = wb[cols]
+        ysub = y_bits[:, cols]
+    else:
+        wsub, ysub = wb, y_bits
+    y_orc, S = oracle.proj(xb, wsub, want_sum=True, threads=threads)
+    wmax = float(np.abs(parity.bf16_to_f64(wb)).max())
+    rep = parity.gate(ysub, y_orc, S, xb, wmax, label=label)
+    say(f"[{label}] elements={rep['elements']} g1_fail={rep['g1_fail']} "
+        f"g2={rep['g2_max_beyond_rounding']:.3g}/{rep['g2_limit']:.3g} "
+        f"diff_frac={rep['d1_diff_frac']:.2e} max_ulp={rep['max_ulp']}")
+    assert rep["ok"], rep
+    return rep
+
+
+def check_exact(label, y_bits, x_cpu, W_cpu, cols=None):
+    """Bitwise equality with the oracle (exact-sum / closed-form inputs)."""
+    xb = wl.bits(x_cpu)
+    wb = wl.bits(W_cpu)
+    if cols is not None:
+        wb = wb[cols]
+        y_bits = y_bits[:, cols]
+    want = oracle.proj(xb, wb)
+    bad = np.argwhere(y_bits != want)
+    say(f"[{label}] exact: {y_bits.size} elements, {len(bad)} mismatches")
+    assert bad.size == 0, f"{label}: first mismatch at {bad[0]}: " \
+        f"{y_bits[tuple(bad[0])]:#06x} vs {want[tuple(bad[0])]:#06x}"
+
+
+def tactic_label(plan, B):
+    t, b = plan.tactic(B)
+    return f"{t.kernel_name} bcap={t.bcap} S={t.split} rows={t.rows} waves={t.waves} wpc={t.wpc} bin={b}"
+
+
+def candidate_tactics(N: int, K: int, bin_: int):
+    """A spread of valid tactics for a bin (every family and split path)."""
+    out = []
+    if bin_ <= 8:
+        for bc in (1, 2, 4, 8):
+            if bc < bin_:
+                continue
+            for rows in (1, 2, 4):
+                for split in (1, 3):
+                    for waves, wpc in ((4, 8), (2, 4), (8, 16), (1, 1), (3, 5)):
+                        out.append(tp.Tactic(tp.KERNEL_STREAM, bc, split, rows, waves, wpc))
+    for bc in (16, 32, 64, 128, 256):
+        if bc < bin_:
+            continue
+        for rows in (1, 2, 4):
+            if bc == 256 and rows > 1:
+                continue
+            for split in (1, 2):
+                for wpc in (0, 3):
+                    out.append(tp.Tactic(tp.KERNEL_MFMA, bc, split, rows, 4, wpc))
+    return out

@@ -10,9 +10,11 @@ G1 (per element): BF16 ulp distance <= 2, or
 G2 (aggregate, error beyond the output's own rounding):
     max_e max(0, |y - S| - ulp(y)/2) <= 0.005 * RMS(y_oracle),
     S being the oracle's unrounded double sum.
-D1 (diagnostic, gated loosely): the fraction of elements that differ from
-    the oracle at all is < 1e-3 (an FP32 kernel differs only at near-ties,
-    ~1e-5..1e-4; a truncating epilogue would differ at ~50%).
+D1 (diagnostic, gated loosely): at most 1e-3 * n + 3 of the n elements
+    differ from the oracle at all (an FP32 kernel differs only at near-ties,
+    ~1e-5..1e-4 of them; a truncating epilogue would differ at ~50%; the
+    constant 3 keeps a single legitimate flip in a few hundred elements from
+    failing a fraction test).
 Exact-sum workloads are compared bit for bit instead.
 """
 from __future__ import annotations
@@ -86,7 +88,8 @@ def gate(y_bits, y_orc_bits, S, x_bits, w_absmax: float, *, label: str = "",
         idx = np.argwhere(~g1_elem)[0]
         rep["worst"] = {"index": [int(i) for i in idx],
                         "gpu": float(yv[tuple(idx)]), "oracle": float(yov[tuple(idx)])}
-    rep["ok"] = (rep["g1_fail"] == 0 and g2 <= rep["g2_limit"] and frac < 1e-3)
+    rep["d1_limit"] = 1e-3 * y.size + 3
+    rep["ok"] = (rep["g1_fail"] == 0 and g2 <= rep["g2_limit"] and ndiff <= rep["d1_limit"])
     return rep
 
 

@@ -1,0 +1,181 @@
+"""CPU tests of the C ABI: symbols, host-only plans, bins and validation.
+
+No compute call is made here (there is no GPU); host-only plans exercise the
+plan logic and every argument check of proj_run up to the launch.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import tp1_skinny_bf16_amd as tp
+from tp1_skinny_bf16_amd import _binding as bd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tp1_proj.h")
+
+SHAPES = [(14560, 7168), (7168, 12288), (49376, 7168)]
+ALL_B = [1, 2, 4, 8, 16, 32, 64, 128, 256]
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(proj_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_binding_exports():
+    assert header_functions() == sorted(tp.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = tp.library()
+    out = subprocess.run(["nm", "-D", "--defined-only", tp.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in header_functions():
+        assert name in exported, f"{name} not exported"
+        assert hasattr(lib, name)
+
+
+def test_strerror_covers_every_status():
+    for code in (tp.PROJ_OK, tp.PROJ_EINVAL, tp.PROJ_EBATCH, tp.PROJ_EALIGN,
+                 tp.PROJ_EHIP, tp.PROJ_ENOMEM, tp.PROJ_ENODEV):
+        assert tp.strerror(code) and tp.strerror(code) != "unknown status"
+    assert tp.strerror(12345) == "unknown status"
+
+
+def _plan_rc(N, K, batches, flags=bd.PLAN_HOST_ONLY):
+    lib = tp.library()
+    arr = (ctypes.c_int * max(1, len(batches)))(*batches)
+    h = ctypes.c_void_p()
+    rc = lib.proj_plan(N, K, arr, len(batches), flags, ctypes.byref(h))
+    if h:
+        lib.proj_free(h)
+    return rc
+
+
+@pytest.mark.parametrize("N,K,batches", [
+    (0, 7168, [1]), (-1, 7168, [1]), (100, 0, [1]), (100, 7164, [1]),
+    (100, 64, []), (100, 64, [2, 1]), (100, 64, [1, 1]), (100, 64, [0]),
+    (100, 64, [257]), (100, 64, list(range(1, 66))),
+])
+def test_plan_rejects_bad_arguments(N, K, batches):
+    assert _plan_rc(N, K, batches) == tp.PROJ_EINVAL
+
+
+def test_plan_rejects_unknown_flags_and_null_out():
+    assert _plan_rc(100, 64, [1], flags=0x80) == tp.PROJ_EINVAL
+    arr = (ctypes.c_int * 1)(1)
+    assert tp.library().proj_plan(100, 64, arr, 1, 1, None) == tp.PROJ_EINVAL
+
+
+def test_bins_follow_the_smallest_key_at_or_above():
+    # the page's _bins: the smallest key >= batch; above the largest key
+    # this library refuses instead of falling back.
+    p = tp.Plan(14560, 7168, [4, 16, 64], host_only=True)
+    assert p.tactic(1)[1] == 4
+    assert p.tactic(4)[1] == 4
+    assert p.tactic(5)[1] == 16
+    assert p.tactic(17)[1] == 64
+    assert p.tactic(64)[1] == 64
+    for bad in (0, -3, 65, 1000):
+        with pytest.raises(tp.ProjError) as e:
+            p.tactic(bad)
+        assert e.value.code == tp.PROJ_EBATCH
+
+
+@pytest.mark.parametrize("N,K", SHAPES + [(1000, 1032), (777, 2056), (33, 8), (5, 12288)])
+def test_every_planned_bin_gets_a_valid_tactic(N, K):
+    p = tp.Plan(N, K, ALL_B, host_only=True)
+    for b in range(1, 257):
+        t, bin_ = p.tactic(b)
+        assert bin_ >= b and t.bcap >= bin_
+        assert t.kernel in (tp.KERNEL_STREAM, tp.KERNEL_MFMA)
+        # setting the chosen tactic back must validate
+        p.set_tactic(bin_, t)
+
+
+def test_set_tactic_validation():
+    p = tp.Plan(14560, 7168, [1, 16], host_only=True)
+    good = tp.Tactic(tp.KERNEL_STREAM, 1, 2, 2, 4, 8)
+    p.set_tactic(1, good)
+    assert p.tactic(1)[0] == good
+    assert p.workspace_bytes >= 2 * 1 * 14560 * 4
+    for bad in [tp.Tactic(tp.KERNEL_STREAM, 1, 1, 3, 4, 8),       # no instance
+                tp.Tactic(tp.KERNEL_STREAM, 1, 1, 1, 9, 8),       # too many waves
+                tp.Tactic(tp.KERNEL_STREAM, 1, 0, 1, 4, 8),       # split 0
+                tp.Tactic(tp.KERNEL_MFMA, 8, 1, 1, 4, 0),         # no MFMA bcap 8
+                tp.Tactic(tp.KERNEL_MFMA, 256, 1, 2, 4, 0),       # too many acc regs
+                tp.Tactic(7, 1, 1, 1, 1, 1)]:
+        with pytest.raises(tp.ProjError):
+            p.set_tactic(1, bad)
+    with pytest.raises(tp.ProjError):                           # bcap < bin
+        p.set_tactic(16, tp.Tactic(tp.KERNEL_STREAM, 8, 1, 1, 4, 8))
+    with pytest.raises(tp.ProjError):                           # not a bin
+        p.set_tactic(3, good)
+    # x for 8 rows of K = 12288 in one slice does not fit the LDS
+    q = tp.Plan(7168, 12288, [8], host_only=True)
+    with pytest.raises(tp.ProjError):
+        q.set_tactic(8, tp.Tactic(tp.KERNEL_STREAM, 8, 1, 1, 4, 8))
+
+
+def test_run_argument_checks_on_a_host_only_plan():
+    p = tp.Plan(128, 256, [1, 8], host_only=True)
+    X, Wp, Y = 0x10000, 0x200000, 0x800000      # never dereferenced
+    assert p.run_ptr(0, X, 256, Wp, Y) == tp.PROJ_OK              # no-op
+    assert p.run_ptr(9, X, 256, Wp, Y) == tp.PROJ_EBATCH
+    assert p.run_ptr(-1, X, 256, Wp, Y) == tp.PROJ_EBATCH
+    assert p.run_ptr(1, 0, 256, Wp, Y) == tp.PROJ_EINVAL
+    assert p.run_ptr(1, X, 256, 0, Y) == tp.PROJ_EINVAL
+    assert p.run_ptr(1, X, 256, Wp, 0) == tp.PROJ_EINVAL
+    assert p.run_ptr(1, X, 255, Wp, Y) == tp.PROJ_EINVAL          # ldx < K
+    assert p.run_ptr(2, X, 260, Wp, Y) == tp.PROJ_EALIGN          # ldx % 8
+    assert p.run_ptr(1, X + 2, 256, Wp, Y) == tp.PROJ_EALIGN
+    assert p.run_ptr(1, X, 256, Wp + 8, Y) == tp.PROJ_EALIGN
+    assert p.run_ptr(1, X, 256, Wp, Y + 4) == tp.PROJ_EALIGN
+    assert p.run_ptr(1, X, 256, Wp, X + 16) == tp.PROJ_EINVAL     # y overlaps x
+    assert p.run_ptr(1, X, 256, Wp, Wp + 4096) == tp.PROJ_EINVAL  # y overlaps W
+    assert p.run_ptr(8, X, 0, Wp, Y) == tp.PROJ_ENODEV            # ldx 0 = K
+    assert p.run_ptr(1, X, 256, Wp, Y) == tp.PROJ_ENODEV
+    lib = tp.library()
+    assert lib.proj_run(None, 1, X, 256, Wp, Y, None) == tp.PROJ_EINVAL
+    lib.proj_free(None)                                           # NULL-safe
+
+
+def test_run_layers_argument_checks():
+    lib = tp.library()
+    pin = tp.Plan(14560, 7168, [64], host_only=True)
+    po = tp.Plan(7168, 12288, [64], host_only=True)
+    bad_o = tp.Plan(7000, 12288, [64], host_only=True)
+    W = (ctypes.c_void_p * 2)(0x100000, 0x200000)
+    Wz = (ctypes.c_void_p * 2)(0x100000, None)
+    X, Y1, Y2 = 0x10000000, 0x20000000, 0x30000000
+    call = lambda a, b, L, B, w=W: lib.proj_run_layers(  # noqa: E731
+        a.handle, b.handle, L, B, ctypes.c_void_p(X), 0, w, w,
+        ctypes.c_void_p(Y1), ctypes.c_void_p(Y2), None)
+    assert call(pin, po, 2, 64) == tp.PROJ_ENODEV
+    assert call(pin, po, 0, 64) == tp.PROJ_OK
+    assert call(pin, po, 2, 65) == tp.PROJ_EBATCH
+    assert call(pin, bad_o, 2, 64) == tp.PROJ_EINVAL     # o_proj N != K_in
+    assert call(po, pin, 2, 64) == tp.PROJ_EINVAL        # wrong chain order
+    assert call(pin, po, 2, 64, Wz) == tp.PROJ_EINVAL    # a NULL weight
+    assert call(pin, po, -1, 64) == tp.PROJ_EINVAL
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(bd, "_LIB", None)
+    monkeypatch.setattr(bd, "LIB_PATH", str(tmp_path / "absent.so"))
+    with pytest.raises(ImportError):
+        bd.library()
+
+
+def test_product_package_never_touches_the_oracle():
+    pkg = os.path.join(ROOT, "tp1_skinny_bf16_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".cpp", ".hpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert not re.search(r"\boracle\b", text), f"{f} mentions the oracle"

@@ -40,7 +40,7 @@ def test_many_flips_fail_d1():
     n = 2000
     y = np.full((1, n), 0x3F80, dtype=np.uint16)
     yo = y.copy()
-    yo[0, :10] = 0x3F81                         # 0.5% differ
+    yo[0, :10] = 0x3F81                         # 10 > 0.001 * 2000 + 3 differ
     S = np.full((1, n), 1.0)
     xb = np.full((1, 4), 0x3F80, dtype=np.uint16)
     rep = parity.gate(y, yo, S, xb, 0.02)
@@ -50,3 +50,12 @@ def test_many_flips_fail_d1():
 def test_nonfinite_gpu_output_fails():
     rep = _case([0x7FC0], [0x3F80], [1.0])
     assert rep["g1_fail"] == 1
+
+
+def test_single_flip_in_a_small_sample_passes():
+    y = np.full((1, 231), 0x3F80, dtype=np.uint16)
+    yo = y.copy()
+    yo[0, 5] = 0x3F81
+    S = np.full((1, 231), 1.0 + 2 ** -8)
+    rep = parity.gate(y, yo, S, np.full((1, 4), 0x3F80, dtype=np.uint16), 0.02)
+    assert rep["ok"], rep

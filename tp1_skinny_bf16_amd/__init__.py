@@ -1,0 +1,14 @@
+"""TP1 BF16 decode projection for MI355X (gfx950).
+
+y[B, N] = x[B, K] . W^T with BF16 x and W (nn.Linear N x K layout), FP32
+accumulation and BF16 output, for decode batches B = 1..256, as the TP1 linear
+of the vLLM API page "vllm.models.kimi_k3.nvidia.specialized_decode.runtime.dep"
+(section "DepProjection") defines it.  The work runs in hand-written HIP
+kernels behind the C ABI of include/tp1_proj.h; this package is the thin
+Python binding (torch supplies device memory and streams only).
+"""
+from ._binding import (EXPORTS, KERNEL_MFMA, KERNEL_NAMES, KERNEL_STREAM,  # noqa: F401
+                       LIB_PATH, MAX_BATCH, MAX_BATCHES, PROJ_EALIGN, PROJ_EBATCH,
+                       PROJ_EHIP, PROJ_EINVAL, PROJ_ENODEV, PROJ_ENOMEM, PROJ_OK,
+                       Plan, ProjError, Tactic, library, read_probe, strerror)
+from .layers import LayerStack  # noqa: F401

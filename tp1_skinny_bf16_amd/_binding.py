@@ -1,0 +1,241 @@
+"""ctypes binding of the C ABI in include/tp1_proj.h (argument marshalling only).
+
+Every step of the projection runs in the HIP library libtp1proj.so; this
+module only turns torch tensors into device pointers and streams.  If the
+library is not built, importing the binding raises: there is no CPU or
+PyTorch fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libtp1proj.so")
+
+PROJ_OK = 0
+PROJ_EINVAL = -1
+PROJ_EBATCH = -2
+PROJ_EALIGN = -3
+PROJ_EHIP = -4
+PROJ_ENOMEM = -5
+PROJ_ENODEV = -6
+
+KERNEL_STREAM = 1
+KERNEL_MFMA = 2
+KERNEL_NAMES = {KERNEL_STREAM: "stream", KERNEL_MFMA: "mfma"}
+
+PLAN_HOST_ONLY = 0x1
+MAX_BATCH = 256
+MAX_BATCHES = 64
+
+# every symbol include/tp1_proj.h declares
+EXPORTS = ("proj_plan", "proj_run", "proj_free", "proj_strerror",
+           "proj_plan_tactic", "proj_plan_set_tactic",
+           "proj_plan_workspace_bytes", "proj_read_probe", "proj_run_layers",
+           "proj_plan_kernel_name")
+
+
+class ProjError(RuntimeError):
+    def __init__(self, code: int, what: str = ""):
+        self.code = code
+        msg = _lib().proj_strerror(code).decode() if _LIB is not None else str(code)
+        super().__init__(f"{what}: {msg} ({code})" if what else f"{msg} ({code})")
+
+
+class _Tactic(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_int), ("bcap", ctypes.c_int),
+                ("split", ctypes.c_int), ("rows", ctypes.c_int),
+                ("waves", ctypes.c_int), ("wpc", ctypes.c_int)]
+
+
+@dataclasses.dataclass(frozen=True)
+class Tactic:
+    kernel: int
+    bcap: int
+    split: int
+    rows: int
+    waves: int
+    wpc: int
+
+    @property
+    def kernel_name(self) -> str:
+        return KERNEL_NAMES.get(self.kernel, str(self.kernel))
+
+    def as_dict(self) -> dict:
+        d = dataclasses.asdict(self)
+        d["kernel"] = self.kernel_name
+        return d
+
+    def _c(self) -> _Tactic:
+        return _Tactic(self.kernel, self.bcap, self.split, self.rows, self.waves,
+                       self.wpc)
+
+
+_LIB = None
+
+
+def _lib():
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is not built: run __graft_entry__.build() (or "
+            "python tp1_skinny_bf16_amd/build.py); there is no fallback path")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp = ctypes.c_void_p
+    lib.proj_plan.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_int),
+                              ctypes.c_int, ctypes.c_uint, ctypes.POINTER(vp)]
+    lib.proj_plan.restype = ctypes.c_int
+    lib.proj_run.argtypes = [vp, ctypes.c_int, vp, ctypes.c_long, vp, vp, vp]
+    lib.proj_run.restype = ctypes.c_int
+    lib.proj_free.argtypes = [vp]
+    lib.proj_free.restype = None
+    lib.proj_strerror.argtypes = [ctypes.c_int]
+    lib.proj_strerror.restype = ctypes.c_char_p
+    lib.proj_plan_tactic.argtypes = [vp, ctypes.c_int, ctypes.POINTER(_Tactic),
+                                     ctypes.POINTER(ctypes.c_int)]
+    lib.proj_plan_tactic.restype = ctypes.c_int
+    lib.proj_plan_set_tactic.argtypes = [vp, ctypes.c_int, ctypes.POINTER(_Tactic)]
+    lib.proj_plan_set_tactic.restype = ctypes.c_int
+    lib.proj_plan_workspace_bytes.argtypes = [vp]
+    lib.proj_plan_workspace_bytes.restype = ctypes.c_size_t
+    lib.proj_plan_kernel_name.argtypes = [vp, ctypes.c_int, ctypes.c_char_p, ctypes.c_size_t]
+    lib.proj_plan_kernel_name.restype = ctypes.c_int
+    lib.proj_run_layers.argtypes = [vp, vp, ctypes.c_int, ctypes.c_int, vp, ctypes.c_long,
+                                    ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp, vp]
+    lib.proj_run_layers.restype = ctypes.c_int
+    lib.proj_read_probe.argtypes = [vp, ctypes.c_size_t, vp, ctypes.c_int, vp]
+    lib.proj_read_probe.restype = ctypes.c_int
+    _LIB = lib
+    return lib
+
+
+def library():
+    """The loaded ctypes library (raises ImportError when not built)."""
+    return _lib()
+
+
+def strerror(code: int) -> str:
+    return _lib().proj_strerror(code).decode()
+
+
+def _check(rc: int, what: str):
+    if rc != PROJ_OK:
+        raise ProjError(rc, what)
+
+
+def _stream_handle(stream) -> int:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+class Plan:
+    """A plan for an N x K BF16 weight and a list of batch sizes.
+
+    Mirrors the page's DepProjection: `run(x, W, out)` writes
+    y = x . W^T into `out` (BF16 [B, N]) and returns it.
+    """
+
+    def __init__(self, N: int, K: int, batches, *, host_only: bool = False):
+        self.N, self.K = int(N), int(K)
+        self.batches = tuple(int(b) for b in batches)
+        arr = (ctypes.c_int * max(1, len(self.batches)))(*self.batches)
+        h = ctypes.c_void_p()
+        rc = _lib().proj_plan(self.N, self.K, arr, len(self.batches),
+                              PLAN_HOST_ONLY if host_only else 0, ctypes.byref(h))
+        _check(rc, f"proj_plan(N={N}, K={K}, batches={self.batches})")
+        self._h = h
+        self.host_only = host_only
+
+    def close(self):
+        h, self._h = getattr(self, "_h", None), None
+        if h:
+            _lib().proj_free(h)
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+    @property
+    def handle(self):
+        return self._h
+
+    @property
+    def workspace_bytes(self) -> int:
+        return int(_lib().proj_plan_workspace_bytes(self._h))
+
+    def tactic(self, B: int):
+        """(Tactic, bin) proj_run would use for batch B."""
+        t = _Tactic()
+        b = ctypes.c_int()
+        _check(_lib().proj_plan_tactic(self._h, int(B), ctypes.byref(t), ctypes.byref(b)),
+               f"proj_plan_tactic(B={B})")
+        return Tactic(t.kernel, t.bcap, t.split, t.rows, t.waves, t.wpc), b.value
+
+    def kernel_name(self, B: int) -> str:
+        """Kernel instance(s) proj_run launches for batch B (profiler names)."""
+        buf = ctypes.create_string_buffer(128)
+        _check(_lib().proj_plan_kernel_name(self._h, int(B), buf, 128),
+               f"proj_plan_kernel_name(B={B})")
+        return buf.value.decode()
+
+    def set_tactic(self, bin_: int, tactic: Tactic):
+        c = tactic._c()
+        _check(_lib().proj_plan_set_tactic(self._h, int(bin_), ctypes.byref(c)),
+               f"proj_plan_set_tactic(bin={bin_}, {tactic})")
+
+    def run_ptr(self, B: int, x_ptr: int, ldx: int, w_ptr: int, y_ptr: int,
+                stream: int = 0) -> int:
+        """Raw call: returns the status code instead of raising."""
+        return _lib().proj_run(self._h, int(B), ctypes.c_void_p(x_ptr), int(ldx),
+                               ctypes.c_void_p(w_ptr), ctypes.c_void_p(y_ptr),
+                               ctypes.c_void_p(stream))
+
+    def run(self, x, W, out=None, *, stream=None):
+        """y[B, N] = x[B, K] . W^T on the GPU; x may have a row stride > K."""
+        import torch
+        if x.dtype != torch.bfloat16 or W.dtype != torch.bfloat16:
+            raise TypeError("x and W must be bfloat16")
+        if x.dim() != 2 or W.dim() != 2 or x.shape[1] != self.K or \
+                tuple(W.shape) != (self.N, self.K):
+            raise ValueError(f"shapes x{tuple(x.shape)} W{tuple(W.shape)} do not "
+                             f"match the plan ({self.N} x {self.K})")
+        if not (x.is_cuda and W.is_cuda):
+            raise ValueError("x and W must be device tensors")
+        if x.stride(1) != 1 or not W.is_contiguous():
+            raise ValueError("x needs unit column stride and W must be contiguous")
+        B = x.shape[0]
+        if out is None:
+            out = torch.empty((B, self.N), dtype=torch.bfloat16, device=x.device)
+        if tuple(out.shape) != (B, self.N) or not out.is_contiguous() or \
+                out.dtype != torch.bfloat16:
+            raise ValueError("out must be a contiguous bfloat16 [B, N] tensor")
+        ldx = x.stride(0) if B > 1 else self.K
+        rc = self.run_ptr(B, x.data_ptr(), ldx, W.data_ptr(), out.data_ptr(),
+                          _stream_handle(stream))
+        _check(rc, f"proj_run(B={B})")
+        return out
+
+
+def read_probe(buf, sink, waves_per_cu: int = 0, stream=None):
+    """Enqueue the streaming-read probe over tensor `buf` (measurement aid)."""
+    rc = _lib().proj_read_probe(ctypes.c_void_p(buf.data_ptr()),
+                                buf.numel() * buf.element_size(),
+                                ctypes.c_void_p(sink.data_ptr()), int(waves_per_cu),
+                                ctypes.c_void_p(_stream_handle(stream)))
+    _check(rc, "proj_read_probe")

@@ -1,0 +1,582 @@
+// kernels.hip -- gfx950 kernels of the TP1 decode projection y = x . W^T.
+//
+// The operation is the TP1 linear of the vLLM API page "vllm.models.kimi_k3.
+// nvidia.specialized_decode.runtime.dep" (section "DepProjection"; the
+// page's opening text fixes BF16 inputs/outputs, FP32 accumulation and a
+// free split-K summation order).  W is N x K row-major (nn.Linear), x is
+// B x K with row stride ldx, y is B x N contiguous.
+//
+// Kernels:
+//   stream_kernel  small batches.  The weight is streamed once from HBM with
+//                  128-bit loads, lanes laid along K (a wave reads 1 KB of a
+//                  row per load), the K slice of x staged once per workgroup
+//                  in LDS, exact BF16 -> FP32 unpacking and IEEE FP32 fused
+//                  multiply-adds, then a fixed-order DPP reduction across the
+//                  64 lanes.  Each wave owns a contiguous range of rows and
+//                  keeps a ring of weight loads in flight across rows.
+//   mfma_kernel    larger batches.  v_mfma_f32_16x16x32_bf16 tiles with x as
+//                  the A operand (batch rows) and W as the B operand (output
+//                  columns), both loaded straight into registers in operand
+//                  layout, FP32 accumulators.
+//   splitk_reduce  when K is split across workgroups: sums the FP32 slices
+//                  in the fixed order s = 0..S-1 and rounds to BF16 (no
+//                  atomics, so results are bitwise reproducible).
+//   read_probe     measurement aid: a plain streaming read of a buffer.
+// Every output is rounded once from FP32 to BF16, nearest-even.
+#include "kernels.hpp"
+
+#include <cstdio>
+
+#include "plan.hpp"
+
+namespace tp1 {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// 128-bit loads.  The weight is read exactly once per call, so its loads are
+// marked non-temporal; x and staging data use ordinary loads.
+__device__ __forceinline__ u32x4 load_stream(const uint16_t *p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
+__device__ __forceinline__ u32x4 load_cached(const uint16_t *p) {
+    return *reinterpret_cast<const u32x4 *>(p);
+}
+
+// FP32 -> BF16, round to nearest, ties to even; NaN -> canonical quiet NaN.
+__device__ __forceinline__ uint16_t to_bf16(float f) {
+    unsigned u = __float_as_uint(f);
+    if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0;
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+// Wave-uniform value: the compiler then keeps what derives from it in SGPRs
+// and every branch on it scalar.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Exact BF16 -> FP32 of the two halves of a packed pair.
+__device__ __forceinline__ float bf_lo(unsigned u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf_hi(unsigned u) { return __uint_as_float(u & 0xFFFF0000u); }
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// Sum over the 64 lanes of a wave in a fixed tree (so results are bitwise
+// reproducible): DPP butterflies inside each 16-lane row (xor 1, xor 2,
+// half-row mirror, row mirror), then the four row sums read from lanes
+// 0, 16, 32, 48 and added in that order.  Returns the wave-uniform total.
+__device__ __forceinline__ float wave_sum(float v) {
+    v += dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+    v += dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+    v += dpp<0x141>(v);  // row_half_mirror
+    v += dpp<0x140>(v);  // row_mirror
+    const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return ((a + b) + c) + d;
+}
+
+// ---------------------------------------------------------------------------
+// Weight-stream kernel (small batches).
+//
+// Workgroup g owns rows [N*g/G, N*(g+1)/G) of W (so workgroups differ by at
+// most one row) for one K slice.  Its rows are cut into groups of R rows and
+// each group's K slice into 512-wide chunks; the (group, chunk) steps are
+// split evenly over the workgroup's waves, each wave taking a contiguous run
+// (so every wave loads the same number of 1 KB pieces, to within one).  A
+// step reads R rows x 1 KB with lanes laid along K.  A group that a wave
+// covers entirely is reduced over the wave's 64 lanes and written out; a
+// group cut by a wave boundary leaves per-wave partial sums in LDS that are
+// added in wave order after one barrier at the end.  Loads form a ring of P
+// steps issued ahead of use and are unconditional: positions past the
+// wave's last step or the workgroup's last row are clamped onto data
+// already read (a cache hit) and discarded.  Arithmetic is exact BF16 ->
+// FP32 unpacking and IEEE FP32 fused multiply-adds.
+// ---------------------------------------------------------------------------
+constexpr int kStreamMaxWaves = 8;
+
+struct StreamArgs {
+    const uint16_t *x;
+    long ldx;
+    const uint16_t *W;
+    uint16_t *y;
+    float *ws;
+    int N, K, B;
+    int ks;   // K elements per slice (multiple of 8)
+    int ksp;  // LDS row pitch of the staged x slice (multiple of 512)
+    int S;    // number of K slices (gridDim.y)
+};
+
+// Wave whose run [q_v, q_v+1) of T steps split over NW waves holds step q.
+__device__ __forceinline__ int wave_of_step(int q, int T, int NW) {
+    return (int)(((long)(q + 1) * NW + T - 1) / T) - 1;
+}
+
+template <int BC, int R, int P>
+__global__ __launch_bounds__(512) void stream_kernel(StreamArgs a) {
+    extern __shared__ __align__(16) uint16_t xs[];
+    __shared__ float part[kStreamMaxWaves][2][R * BC];  // [wave][head/tail][r*BC+b]
+
+    const int s = blockIdx.y;
+    const int k0 = s * a.ks;
+    const int klen = min(a.K - k0, a.ks);
+    const int NW = uniform(blockDim.x >> 6);
+    const int wave = uniform(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int row0 = (int)((long)a.N * blockIdx.x / gridDim.x);
+    const int rows = (int)((long)a.N * (blockIdx.x + 1) / gridDim.x) - row0;
+    const int C = (klen + 511) >> 9;           // 512-wide chunks per row
+    const int Gb = (rows + R - 1) / R;         // row groups of this workgroup
+    const int Tb = Gb * C;                     // steps of this workgroup
+    const int q0 = (int)((long)Tb * wave / NW);
+    const int q1 = (int)((long)Tb * (wave + 1) / NW);
+    const int T = q1 - q0;                     // steps of this wave
+    const bool ragged = (klen & 511) != 0;
+    const int lk = lane * 8;
+    const uint16_t *wblk = a.W + (size_t)row0 * a.K + k0;
+
+    u32x4 buf[P][R];
+    // Load cursor: (group, chunk) of the next step to load; it stops at the
+    // wave's last step, so the ring's tail re-reads it instead of running on.
+    int lt = 0, lg = q0 / C, lc = q0 - (q0 / C) * C;
+    auto load_step = [&](u32x4 (&dst)[R]) {
+        const int kk = min(lc * 512 + lk, klen - 8);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            const int row = min(lg * R + r, rows - 1);
+            dst[r] = load_stream(wblk + (size_t)row * a.K + kk);
+        }
+        if (lt < T - 1) {
+            ++lt;
+            if (++lc == C) { lc = 0; ++lg; }
+        }
+    };
+    // Weight loads go out first; x staging overlaps their latency.
+    if (T > 0) {
+#pragma unroll
+        for (int j = 0; j < P; ++j) load_step(buf[j]);
+    }
+
+    // Stage x[0:BC][k0 : k0 + ksp] into LDS, zero past B and past the slice.
+    const int vpr = a.ksp >> 3;  // 16-byte vectors per staged row
+    for (int i = threadIdx.x; i < BC * vpr; i += blockDim.x) {
+        const int b = i / vpr;
+        const int kk = (i - b * vpr) << 3;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (b < a.B && kk < klen) v = load_cached(a.x + (size_t)b * a.ldx + k0 + kk);
+        *reinterpret_cast<u32x4 *>(xs + b * a.ksp + kk) = v;
+    }
+    __syncthreads();
+
+    auto store_out = [&](int row, int b, float v) {
+        if (a.S == 1)
+            a.y[(size_t)b * a.N + row] = to_bf16(v);
+        else
+            a.ws[((size_t)s * a.B + b) * a.N + row] = v;
+    };
+
+    if (T > 0) {
+        float acc[R][BC];
+#pragma unroll
+        for (int r = 0; r < R; ++r)
+#pragma unroll
+            for (int b = 0; b < BC; ++b) acc[r][b] = 0.f;
+        int cg = q0 / C, cc = q0 - (q0 / C) * C;  // (group, chunk) being computed
+        for (int t0 = 0; t0 < T; t0 += P) {
+#pragma unroll
+            for (int j = 0; j < P; ++j) {
+                if (t0 + j < T) {
+                    u32x4 w[R];
+#pragma unroll
+                    for (int r = 0; r < R; ++r) w[r] = buf[j][r];
+                    if (ragged && cc == C - 1) {
+                        const bool dead = cc * 512 + lk >= klen;  // past the slice
+#pragma unroll
+                        for (int r = 0; r < R; ++r)
+                            w[r] = dead ? u32x4{0u, 0u, 0u, 0u} : w[r];
+                    }
+                    const int kk = cc * 512 + lk;
+#pragma unroll
+                    for (int b = 0; b < BC; ++b) {
+                        const u32x4 xv = *reinterpret_cast<const u32x4 *>(xs + b * a.ksp + kk);
+                        const float x0 = bf_lo(xv.x), x1 = bf_hi(xv.x), x2 = bf_lo(xv.y),
+                                    x3 = bf_hi(xv.y), x4 = bf_lo(xv.z), x5 = bf_hi(xv.z),
+                                    x6 = bf_lo(xv.w), x7 = bf_hi(xv.w);
+#pragma unroll
+                        for (int r = 0; r < R; ++r) {
+                            float t = acc[r][b];
+                            t = __builtin_fmaf(bf_lo(w[r].x), x0, t);
+                            t = __builtin_fmaf(bf_hi(w[r].x), x1, t);
+                            t = __builtin_fmaf(bf_lo(w[r].y), x2, t);
+                            t = __builtin_fmaf(bf_hi(w[r].y), x3, t);
+                            t = __builtin_fmaf(bf_lo(w[r].z), x4, t);
+                            t = __builtin_fmaf(bf_hi(w[r].z), x5, t);
+                            t = __builtin_fmaf(bf_lo(w[r].w), x6, t);
+                            t = __builtin_fmaf(bf_hi(w[r].w), x7, t);
+                            acc[r][b] = t;
+                        }
+                    }
+                }
+                load_step(buf[j]);  // refill this slot P steps ahead
+                if (t0 + j < T) {
+                    if (cc == C - 1 || t0 + j == T - 1) {
+                        // The group ends here or the wave's run does: reduce each
+                        // (row, batch) over the wave; lane r*BC + b keeps (r, b).
+                        float mine = 0.f;
+#pragma unroll
+                        for (int r = 0; r < R; ++r)
+#pragma unroll
+                            for (int b = 0; b < BC; ++b) {
+                                const float v = wave_sum(acc[r][b]);
+                                if (lane == r * BC + b) mine = v;
+                                acc[r][b] = 0.f;
+                            }
+                        const bool started_here = cg * C >= q0;
+                        const int r = lane / BC, b = lane - (lane / BC) * BC;
+                        if (lane < R * BC) {
+                            if (cc == C - 1 && started_here) {
+                                const int row = cg * R + r;
+                                if (row < rows && b < a.B) store_out(row0 + row, b, mine);
+                            } else {
+                                part[wave][started_here ? 1 : 0][lane] = mine;
+                            }
+                        }
+                    }
+                    if (++cc == C) { cc = 0; ++cg; }
+                }
+            }
+        }
+    }
+
+    // Groups cut by a wave boundary: add the waves' partial sums in wave order.
+    __syncthreads();
+    const int per = R * BC;
+    const int tid = threadIdx.x;
+    if (tid < (NW - 1) * per) {
+        const int i = tid / per + 1;  // boundary between waves i-1 and i
+        const int e = tid - (i - 1) * per;
+        const int qi = (int)((long)Tb * i / NW);
+        const int qp = (int)((long)Tb * (i - 1) / NW);
+        const int g = qi / C;
+        const bool split = qi < Tb && (qi - g * C) != 0;
+        const bool seen = i > 1 && qp / C == g && (qp - (qp / C) * C) != 0;
+        if (split && !seen) {
+            const int wlo = wave_of_step(g * C, Tb, NW);
+            const int whi = wave_of_step(g * C + C - 1, Tb, NW);
+            float sum = 0.f;
+            for (int v = wlo; v <= whi; ++v) {
+                const int qv = (int)((long)Tb * v / NW);
+                const int qv1 = (int)((long)Tb * (v + 1) / NW);
+                if (qv == qv1) continue;
+                sum += part[v][g * C < qv ? 0 : 1][e];
+            }
+            const int r = e / BC, b = e - (e / BC) * BC;
+            const int row = g * R + r;
+            if (row < rows && b < a.B) store_out(row0 + row, b, sum);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// MFMA kernel (larger batches).
+// v_mfma_f32_16x16x32_bf16 operand layout: lane l supplies row (l % 16) of
+// the A operand and column (l % 16) of the B operand, each with 8 K values
+// of K group (l / 16); the accumulator lane l holds rows 4*(l/16) + 0..3 of
+// column l % 16.  The K order inside a group only permutes the sum, so each
+// lane simply loads 8 consecutive K of its row.  x is the A operand (batch
+// rows), W the B operand (output columns); a wave owns a contiguous range of
+// 16*NT-column units and walks K in 32-wide steps with a ring of P steps of
+// unconditional loads in flight (rows past B or N are clamped onto valid
+// data and their results discarded).
+// ---------------------------------------------------------------------------
+struct MfmaArgs {
+    const uint16_t *x;
+    long ldx;
+    const uint16_t *W;
+    uint16_t *y;
+    float *ws;
+    int N, K, B;
+    int ks;    // K elements per slice (multiple of 32)
+    int upw;   // N units (16*NT columns) per wave
+    int S;
+};
+
+template <int MT, int NT, int P>
+__global__ __launch_bounds__(256) void mfma_kernel(MfmaArgs a) {
+    const int lane = threadIdx.x & 63;
+    const int gw = blockIdx.x * uniform(blockDim.x >> 6) + uniform(threadIdx.x >> 6);
+    const int s = blockIdx.y;
+    const int k0 = s * a.ks;
+    const int klen = min(a.K - k0, a.ks);
+    const int U = (a.N + 16 * NT - 1) / (16 * NT);
+    const int u_begin = gw * a.upw;
+    const int u_end = min(U, u_begin + a.upw);
+    if (u_begin >= u_end) return;
+    const int C = (klen + 31) >> 5;
+    const int T = (u_end - u_begin) * C;
+    const bool ragged = (klen & 31) != 0;
+    const int lrow = lane & 15, lgrp = lane >> 4;
+
+    const uint16_t *xrow[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+        xrow[m] = a.x + (size_t)min(m * 16 + lrow, a.B - 1) * a.ldx + k0;
+    const uint16_t *wslice = a.W + k0;
+
+    u32x4 wb[P][NT];
+    u32x4 xb[P][MT];
+    f32x4 acc[MT][NT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+#pragma unroll
+        for (int n = 0; n < NT; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    int lt = 0, lu = u_begin, lc = 0;
+    auto load_step = [&](u32x4 (&w)[NT], u32x4 (&xx)[MT]) {
+        const int kk = min(lc * 32 + lgrp * 8, klen - 8);
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+            const int col = min(lu * 16 * NT + n * 16 + lrow, a.N - 1);
+            w[n] = load_stream(wslice + (size_t)col * a.K + kk);
+        }
+#pragma unroll
+        for (int m = 0; m < MT; ++m) xx[m] = load_cached(xrow[m] + kk);
+        if (lt < T - 1) {
+            ++lt;
+            if (++lc == C) { lc = 0; ++lu; }
+        }
+    };
+
+#pragma unroll
+    for (int j = 0; j < P; ++j) load_step(wb[j], xb[j]);
+
+    int cu = u_begin, cc = 0;
+    for (int t0 = 0; t0 < T; t0 += P) {
+#pragma unroll
+        for (int j = 0; j < P; ++j) {
+            if (t0 + j < T) {
+                u32x4 w[NT];
+#pragma unroll
+                for (int n = 0; n < NT; ++n) w[n] = wb[j][n];
+                if (ragged && cc == C - 1) {
+                    const bool dead = cc * 32 + lgrp * 8 >= klen;  // past the slice
+#pragma unroll
+                    for (int n = 0; n < NT; ++n)
+                        w[n] = dead ? u32x4{0u, 0u, 0u, 0u} : w[n];
+                }
+#pragma unroll
+                for (int m = 0; m < MT; ++m)
+#pragma unroll
+                    for (int n = 0; n < NT; ++n)
+                        acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8_t, xb[j][m]),
+                            __builtin_bit_cast(bf16x8_t, w[n]), acc[m][n], 0, 0, 0);
+            }
+            load_step(wb[j], xb[j]);
+            if (t0 + j < T) {
+                if (cc == C - 1) {
+#pragma unroll
+                    for (int m = 0; m < MT; ++m)
+#pragma unroll
+                        for (int n = 0; n < NT; ++n) {
+                            const int col = cu * 16 * NT + n * 16 + lrow;
+#pragma unroll
+                            for (int v = 0; v < 4; ++v) {
+                                const int row = m * 16 + lgrp * 4 + v;
+                                if (row < a.B && col < a.N) {
+                                    if (a.S == 1)
+                                        a.y[(size_t)row * a.N + col] = to_bf16(acc[m][n][v]);
+                                    else
+                                        a.ws[((size_t)s * a.B + row) * a.N + col] = acc[m][n][v];
+                                }
+                            }
+                            acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+                        }
+                }
+                if (++cc == C) { cc = 0; ++cu; }
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Fixed-order split-K reduction: y[i] = bf16( sum_{s=0}^{S-1} ws[s][i] ).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void splitk_reduce(const float *ws, uint16_t *y,
+                                                     long count, int S) {
+    const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= count) return;
+    float acc = ws[i];
+    for (int s = 1; s < S; ++s) acc += ws[(size_t)s * count + i];
+    y[i] = to_bf16(acc);
+}
+
+// ---------------------------------------------------------------------------
+// Streaming-read probe.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void read_probe(const u32x4 *buf, size_t n16,
+                                                  float *sink) {
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    unsigned acc = 0;
+    for (; i + 7 * stride < n16; i += 8 * stride) {
+        u32x4 v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = __builtin_nontemporal_load(buf + i + j * stride);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc ^= v[j].x ^ v[j].y ^ v[j].z ^ v[j].w;
+    }
+    for (; i < n16; i += stride) {
+        const u32x4 v = buf[i];
+        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+    for (int o = 32; o > 0; o >>= 1) acc ^= __shfl_xor(acc, o);
+    if ((threadIdx.x & 63) == 0)
+        sink[(blockIdx.x * blockDim.x + threadIdx.x) >> 6] = __uint_as_float(acc);
+}
+
+// ---------------------------------------------------------------------------
+// Host-side dispatch.
+// ---------------------------------------------------------------------------
+namespace {
+
+int ceil_div_i(long a, long b) { return (int)((a + b - 1) / b); }
+
+// Weight loads in flight per lane: 16 for narrow batches, fewer when the
+// accumulators of a wide batch need the registers.
+constexpr int stream_ring(int BC, int R) {
+    return (BC >= 8 ? 8 : (BC >= 4 ? 12 : 16)) / R > 1
+               ? (BC >= 8 ? 8 : (BC >= 4 ? 12 : 16)) / R
+               : 2;
+}
+
+// Steps of loads in flight for the MFMA kernel (fewer as operands grow).
+constexpr int mfma_ring(int MT, int NT) {
+    return MT + NT <= 2 ? 8 : (MT + NT <= 3 ? 6 : (MT + NT <= 5 ? 4 : (MT + NT <= 8 ? 2 : 1)));
+}
+
+template <int BC, int R>
+hipError_t launch_stream_inst(const LaunchShape &sh, const proj_tactic_t &t,
+                              hipStream_t stream) {
+    constexpr int P = stream_ring(BC, R);
+    const int ks = slice_len(sh.K, t);
+    const int S = slice_count(sh.K, t);
+    const int ksp = ceil_div_i(ks, kStreamChunk) * kStreamChunk;
+    const int nw = std::min(t.waves, kStreamMaxWaves);
+    // workgroups: wpc waves per compute unit over the S slices, at most one
+    // per row
+    long g = (long)sh.num_cus * t.wpc / (nw * (long)S);
+    g = std::max(1L, std::min(g, (long)sh.N));
+    const size_t lds = (size_t)BC * ksp * 2;
+
+    // Dynamic LDS above 64 KB has to be allowed per kernel; raise the limit
+    // once per instance to the largest size launched so far.
+    static size_t lds_allowed = 64 * 1024;
+    if (lds > lds_allowed) {
+        hipError_t e = hipFuncSetAttribute(
+            reinterpret_cast<const void *>(&stream_kernel<BC, R, P>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        lds_allowed = lds;
+    }
+    StreamArgs a{sh.x, sh.ldx, sh.W, sh.y, sh.ws, sh.N, sh.K, sh.B, ks, ksp, S};
+    hipLaunchKernelGGL((stream_kernel<BC, R, P>), dim3((unsigned)g, S), dim3(nw * 64), lds,
+                       stream, a);
+    return hipGetLastError();
+}
+
+template <int MT, int NT>
+hipError_t launch_mfma_inst(const LaunchShape &sh, const proj_tactic_t &t,
+                            hipStream_t stream) {
+    constexpr int P = mfma_ring(MT, NT);
+    const int ks = slice_len(sh.K, t);
+    const int S = slice_count(sh.K, t);
+    const int U = ceil_div_i(sh.N, 16 * NT);
+    int upw = 1;
+    if (t.wpc > 0) {
+        const long tw0 = std::max(1L, (long)sh.num_cus * t.wpc / S);
+        upw = ceil_div_i(U, tw0);
+    }
+    const int tw = ceil_div_i(U, upw);
+    const int nw = std::min(t.waves, 4);
+    const int gx = ceil_div_i(tw, nw);
+    MfmaArgs a{sh.x, sh.ldx, sh.W, sh.y, sh.ws, sh.N, sh.K, sh.B, ks, upw, S};
+    hipLaunchKernelGGL((mfma_kernel<MT, NT, P>), dim3(gx, S), dim3(nw * 64), 0,
+                       stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_stream(const LaunchShape &sh, const proj_tactic_t &t,
+                         hipStream_t st) {
+#define TP1_STREAM_CASE(BC, R) \
+    if (t.bcap == BC && t.rows == R) return launch_stream_inst<BC, R>(sh, t, st);
+    TP1_STREAM_CASE(1, 1) TP1_STREAM_CASE(1, 2) TP1_STREAM_CASE(1, 4)
+    TP1_STREAM_CASE(2, 1) TP1_STREAM_CASE(2, 2) TP1_STREAM_CASE(2, 4)
+    TP1_STREAM_CASE(4, 1) TP1_STREAM_CASE(4, 2) TP1_STREAM_CASE(4, 4)
+    TP1_STREAM_CASE(8, 1) TP1_STREAM_CASE(8, 2) TP1_STREAM_CASE(8, 4)
+#undef TP1_STREAM_CASE
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_mfma(const LaunchShape &sh, const proj_tactic_t &t, hipStream_t st) {
+#define TP1_MFMA_CASE(BC, NT) \
+    if (t.bcap == BC && t.rows == NT) return launch_mfma_inst<BC / 16, NT>(sh, t, st);
+    TP1_MFMA_CASE(16, 1) TP1_MFMA_CASE(16, 2) TP1_MFMA_CASE(16, 4)
+    TP1_MFMA_CASE(32, 1) TP1_MFMA_CASE(32, 2) TP1_MFMA_CASE(32, 4)
+    TP1_MFMA_CASE(64, 1) TP1_MFMA_CASE(64, 2) TP1_MFMA_CASE(64, 4)
+    TP1_MFMA_CASE(128, 1) TP1_MFMA_CASE(128, 2) TP1_MFMA_CASE(128, 4)
+    TP1_MFMA_CASE(256, 1)
+#undef TP1_MFMA_CASE
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_projection(const LaunchShape &sh, const proj_tactic_t &t,
+                             hipStream_t stream) {
+    hipError_t e;
+    if (t.kernel == PROJ_KERNEL_STREAM)
+        e = launch_stream(sh, t, stream);
+    else if (t.kernel == PROJ_KERNEL_MFMA)
+        e = launch_mfma(sh, t, stream);
+    else
+        return hipErrorInvalidValue;
+    if (e != hipSuccess) return e;
+    const int S = slice_count(sh.K, t);
+    if (S > 1) {
+        const long count = (long)sh.B * sh.N;
+        hipLaunchKernelGGL(splitk_reduce, dim3(ceil_div_i(count, 256)), dim3(256), 0,
+                           stream, sh.ws, sh.y, count, S);
+        e = hipGetLastError();
+    }
+    return e;
+}
+
+int kernel_name(int K, const proj_tactic_t &t, char *buf, size_t len) {
+    if (!buf || len == 0) return -1;
+    const bool split = slice_count(K, t) > 1;
+    int n;
+    if (t.kernel == PROJ_KERNEL_STREAM)
+        n = snprintf(buf, len, "stream_kernel<%d, %d, %d>%s", t.bcap, t.rows,
+                     stream_ring(t.bcap, t.rows), split ? "+splitk_reduce" : "");
+    else
+        n = snprintf(buf, len, "mfma_kernel<%d, %d, %d>%s", t.bcap / 16, t.rows,
+                     mfma_ring(t.bcap / 16, t.rows), split ? "+splitk_reduce" : "");
+    return (n < 0 || (size_t)n >= len) ? -1 : 0;
+}
+
+hipError_t launch_read_probe(const void *buf, size_t bytes, float *sink,
+                             int waves_per_cu, int num_cus, hipStream_t stream) {
+    if (waves_per_cu <= 0) waves_per_cu = 8;
+    const int blocks = std::max(1, num_cus * waves_per_cu / 4);
+    hipLaunchKernelGGL(read_probe, dim3(blocks), dim3(256), 0, stream,
+                       reinterpret_cast<const u32x4 *>(buf), bytes / 16, sink);
+    return hipGetLastError();
+}
+
+}  // namespace tp1

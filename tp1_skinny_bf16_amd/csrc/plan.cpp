@@ -1,0 +1,153 @@
+// plan.cpp -- host-side plan logic (no HIP): checks, bins, tactics.
+//
+// The bin rule is the one of the vLLM API page "vllm.models.kimi_k3.nvidia.
+// specialized_decode.runtime.dep", section "_bins": a batch takes the tactic
+// of the smallest table key at or above it.  The page falls back to the
+// largest key (and to cuBLAS for batches without a split-K tactic); this
+// library has no second backend, so a batch above the largest planned one is
+// an error instead (PROJ_EBATCH), and every planned batch gets a tactic of
+// its own kernels (section "dep_policies" keeps only the split-K ones).
+#include "plan.hpp"
+
+#include <algorithm>
+
+#include "tactics_table.hpp"
+
+namespace tp1 {
+
+static int next_pow2(int v) {
+    int p = 1;
+    while (p < v) p <<= 1;
+    return p;
+}
+
+static int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
+
+int check_plan_args(int N, int K, const int *batches, int n_batches,
+                    unsigned flags) {
+    if (N <= 0 || K <= 0 || (K % 8) != 0) return PROJ_EINVAL;
+    if (!batches || n_batches < 1 || n_batches > PROJ_MAX_BATCHES)
+        return PROJ_EINVAL;
+    if (flags & ~PROJ_PLAN_HOST_ONLY) return PROJ_EINVAL;
+    for (int i = 0; i < n_batches; ++i) {
+        if (batches[i] < 1 || batches[i] > PROJ_MAX_BATCH) return PROJ_EINVAL;
+        if (i > 0 && batches[i] <= batches[i - 1]) return PROJ_EINVAL;
+    }
+    // Keep byte offsets far inside 64 bits (a 2^40-element weight is 2 TB).
+    if ((long)N * (long)K >= (1L << 40)) return PROJ_EINVAL;
+    return PROJ_OK;
+}
+
+int bin_index(const PlanCore &p, int B) {
+    if (B < 1) return -1;
+    for (int i = 0; i < p.nb; ++i)
+        if (B <= p.batches[i]) return i;
+    return -1;
+}
+
+bool tactic_instance_exists(const proj_tactic_t &t) {
+    if (t.kernel == PROJ_KERNEL_STREAM)
+        return (t.bcap == 1 || t.bcap == 2 || t.bcap == 4 || t.bcap == 8) &&
+               (t.rows == 1 || t.rows == 2 || t.rows == 4);
+    if (t.kernel == PROJ_KERNEL_MFMA) {
+        const bool m = t.bcap == 16 || t.bcap == 32 || t.bcap == 64 ||
+                       t.bcap == 128 || t.bcap == 256;
+        const bool n = t.rows == 1 || t.rows == 2 || t.rows == 4;
+        // 256 rows x 2+ N tiles would need 128+ accumulator registers.
+        return m && n && !(t.bcap == 256 && t.rows > 1);
+    }
+    return false;
+}
+
+int slice_len(int K, const proj_tactic_t &t) {
+    const int S = std::max(1, t.split);
+    const int step = t.kernel == PROJ_KERNEL_MFMA ? 32 : 8;
+    int ks = ceil_div(K, S);
+    ks = ceil_div(ks, step) * step;
+    return std::max(ks, step);
+}
+
+int slice_count(int K, const proj_tactic_t &t) {
+    return ceil_div(K, slice_len(K, t));
+}
+
+size_t stream_lds_bytes(int K, const proj_tactic_t &t) {
+    const int ks = slice_len(K, t);
+    const int ksp = ceil_div(ks, kStreamChunk) * kStreamChunk;
+    return (size_t)t.bcap * (size_t)ksp * 2u;
+}
+
+size_t tactic_workspace(int N, int K, const proj_tactic_t &t) {
+    const int S = slice_count(K, t);
+    if (S <= 1) return 0;
+    return (size_t)S * (size_t)t.bcap * (size_t)N * sizeof(float);
+}
+
+int check_tactic(int N, int K, int bin, const proj_tactic_t &t) {
+    if (N <= 0 || K <= 0 || bin < 1) return PROJ_EINVAL;
+    if (!tactic_instance_exists(t)) return PROJ_EINVAL;
+    if (t.bcap < bin) return PROJ_EINVAL;
+    if (t.split < 1 || t.split > 64) return PROJ_EINVAL;
+    if (t.waves < 1 || t.waves > kMaxWaves) return PROJ_EINVAL;
+    if (t.wpc < 0 || t.wpc > 32) return PROJ_EINVAL;
+    if (t.kernel == PROJ_KERNEL_STREAM) {
+        if (t.wpc < 1 || t.waves > 8) return PROJ_EINVAL;
+        if (stream_lds_bytes(K, t) > kLdsBytes) return PROJ_EINVAL;
+    }
+    if (t.kernel == PROJ_KERNEL_MFMA && t.waves > 4) return PROJ_EINVAL;
+    return PROJ_OK;
+}
+
+proj_tactic_t default_tactic(int N, int K, int bin, int num_cus) {
+    proj_tactic_t t{};
+    if (num_cus < 1) num_cus = 256;
+    if (bin <= 8) {
+        // Weight stream on the VALU: x staged in LDS per K slice.  Keep the
+        // slice small enough for two workgroups per compute unit.
+        t.kernel = PROJ_KERNEL_STREAM;
+        t.bcap = next_pow2(bin);
+        t.rows = t.bcap >= 4 ? 2 : 1;
+        t.waves = 4;
+        t.wpc = 8;
+        const size_t budget = 80 * 1024;
+        int S = 1;
+        for (;; ++S) {
+            t.split = S;
+            if (stream_lds_bytes(K, t) <= budget || S >= 16) break;
+        }
+        (void)N;
+        return t;
+    }
+    // MFMA tiles: one wave per N range, split K until the chip is covered.
+    t.kernel = PROJ_KERNEL_MFMA;
+    t.bcap = std::max(16, next_pow2(bin));
+    t.rows = t.bcap >= 256 ? 1 : 2;
+    t.waves = 4;
+    t.wpc = 0;
+    const int units = ceil_div(N, 16 * t.rows);
+    int S = 1;
+    while ((long)units * S < 4L * num_cus && S < 8) ++S;
+    t.split = S;
+    return t;
+}
+
+proj_tactic_t choose_tactic(int N, int K, int bin, int num_cus) {
+    proj_tactic_t t;
+    if (lookup_measured_tactic(N, K, bin, &t) && check_tactic(N, K, bin, t) == PROJ_OK)
+        return t;
+    return default_tactic(N, K, bin, num_cus);
+}
+
+void fill_tactics(PlanCore &p) {
+    for (int i = 0; i < p.nb; ++i)
+        p.tactics[i] = choose_tactic(p.N, p.K, p.batches[i], p.num_cus);
+}
+
+size_t plan_workspace(const PlanCore &p) {
+    size_t ws = 0;
+    for (int i = 0; i < p.nb; ++i)
+        ws = std::max(ws, tactic_workspace(p.N, p.K, p.tactics[i]));
+    return ws;
+}
+
+}  // namespace tp1

@@ -1,0 +1,68 @@
+// plan.hpp -- host-side plan logic of the TP1 projection: argument checks,
+// the per-batch tactic table, the bin rule and workspace sizing.  Pure C++:
+// no HIP header is included here, so this logic builds and runs on a host
+// without a GPU.
+#pragma once
+
+#include <cstddef>
+
+#include "../../include/tp1_proj.h"
+
+namespace tp1 {
+
+// Hardware limits of gfx950 the tactics must respect.
+constexpr int kWave = 64;
+constexpr int kMaxWaves = 16;                 // 1024 threads per workgroup
+constexpr size_t kLdsBytes = 160 * 1024;      // LDS per workgroup on gfx950
+constexpr int kStreamChunk = 512;             // K elements one wave load covers
+
+struct PlanCore {
+    int N = 0, K = 0;
+    int nb = 0;
+    int batches[PROJ_MAX_BATCHES] = {};
+    proj_tactic_t tactics[PROJ_MAX_BATCHES] = {};
+    unsigned flags = 0;
+    int num_cus = 256;                        // compute units of the device
+};
+
+// Argument checks of proj_plan (no device access).
+int check_plan_args(int N, int K, const int *batches, int n_batches,
+                    unsigned flags);
+
+// Index of the bin serving B: the smallest planned batch >= B.  -1 when B is
+// out of 1..max(batches).
+int bin_index(const PlanCore &p, int B);
+
+// True when a compiled kernel instance exists for the tactic's template
+// parameters (kernel, bcap, rows).
+bool tactic_instance_exists(const proj_tactic_t &t);
+
+// Validate a tactic for a shape and bin.  Returns PROJ_OK or PROJ_EINVAL.
+int check_tactic(int N, int K, int bin, const proj_tactic_t &t);
+
+// FP32 split-K workspace bytes a tactic needs (0 when split == 1).
+size_t tactic_workspace(int N, int K, const proj_tactic_t &t);
+
+// K elements per split-K slice for a tactic (rounded to the kernel's step).
+int slice_len(int K, const proj_tactic_t &t);
+
+// Number of K slices actually launched (ceil(K / slice_len)).
+int slice_count(int K, const proj_tactic_t &t);
+
+// LDS bytes a STREAM tactic stages x into.
+size_t stream_lds_bytes(int K, const proj_tactic_t &t);
+
+// The tactic for (N, K, bin): the measured table entry when the shape was
+// measured, else the default rule.
+proj_tactic_t choose_tactic(int N, int K, int bin, int num_cus);
+
+// The default rule alone (exposed for tests).
+proj_tactic_t default_tactic(int N, int K, int bin, int num_cus);
+
+// Fill p.tactics for every planned bin.
+void fill_tactics(PlanCore &p);
+
+// Workspace bytes the whole plan needs.
+size_t plan_workspace(const PlanCore &p);
+
+}  // namespace tp1

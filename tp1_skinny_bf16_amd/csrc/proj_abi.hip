@@ -1,0 +1,255 @@
+// proj_abi.hip -- the C ABI declared in include/tp1_proj.h.
+//
+// proj_plan / proj_run / proj_free follow the vLLM API page
+// "vllm.models.kimi_k3.nvidia.specialized_decode.runtime.dep", section
+// "DepProjection": construction binds a per-batch tactic table, and run(x,
+// out) writes the projection into a caller-owned output.  Here the weight is
+// passed per call (one plan serves every layer of a shape) and the batch is
+// explicit because raw pointers do not carry it.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <new>
+
+#include "../../include/tp1_proj.h"
+#include "kernels.hpp"
+#include "plan.hpp"
+
+struct proj_plan_s {
+    tp1::PlanCore core;
+    int device = -1;
+    size_t lds_limit = tp1::kLdsBytes;
+    void *ws = nullptr;
+    size_t ws_bytes = 0;
+};
+
+namespace {
+
+bool aligned16(const void *p) {
+    return (reinterpret_cast<uintptr_t>(p) & 15u) == 0;
+}
+
+int alloc_workspace(proj_plan_s *p, size_t bytes) {
+    if (bytes <= p->ws_bytes) return PROJ_OK;
+    if (p->core.flags & PROJ_PLAN_HOST_ONLY) {
+        p->ws_bytes = bytes;  // bookkeeping only
+        return PROJ_OK;
+    }
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess) return PROJ_EHIP;
+    if (cur != p->device && hipSetDevice(p->device) != hipSuccess) return PROJ_EHIP;
+    int rc = PROJ_OK;
+    if (p->ws) {
+        if (hipFree(p->ws) != hipSuccess) rc = PROJ_EHIP;  // synchronises
+        p->ws = nullptr;
+        p->ws_bytes = 0;
+    }
+    if (rc == PROJ_OK) {
+        void *mem = nullptr;
+        if (hipMalloc(&mem, bytes) != hipSuccess) {
+            (void)hipGetLastError();
+            rc = PROJ_ENOMEM;
+        } else {
+            p->ws = mem;
+            p->ws_bytes = bytes;
+        }
+    }
+    if (cur != p->device) (void)hipSetDevice(cur);
+    return rc;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *proj_strerror(int code) {
+    switch (code) {
+        case PROJ_OK: return "success";
+        case PROJ_EINVAL: return "invalid argument";
+        case PROJ_EBATCH: return "batch outside the planned range";
+        case PROJ_EALIGN: return "pointer or row stride misaligned (16 bytes / 8 elements)";
+        case PROJ_EHIP: return "HIP runtime error";
+        case PROJ_ENOMEM: return "out of memory";
+        case PROJ_ENODEV: return "plan was built host-only and cannot run";
+        default: return "unknown status";
+    }
+}
+
+int proj_plan(int N, int K, const int *batches, int n_batches, unsigned flags,
+              proj_plan_t **out) {
+    if (!out) return PROJ_EINVAL;
+    *out = nullptr;
+    int rc = tp1::check_plan_args(N, K, batches, n_batches, flags);
+    if (rc != PROJ_OK) return rc;
+    proj_plan_s *p = new (std::nothrow) proj_plan_s;
+    if (!p) return PROJ_ENOMEM;
+    p->core.N = N;
+    p->core.K = K;
+    p->core.nb = n_batches;
+    p->core.flags = flags;
+    for (int i = 0; i < n_batches; ++i) p->core.batches[i] = batches[i];
+    if (!(flags & PROJ_PLAN_HOST_ONLY)) {
+        int dev = -1, cus = 0, lds = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess) {
+            (void)hipGetLastError();
+            delete p;
+            return PROJ_EHIP;
+        }
+        p->device = dev;
+        p->core.num_cus = cus > 0 ? cus : 256;
+        if (lds > 0 && (size_t)lds < p->lds_limit) p->lds_limit = (size_t)lds;
+    }
+    tp1::fill_tactics(p->core);
+    // A device with less LDS per workgroup than the table assumes: split K
+    // further until the staged x slice fits.
+    for (int i = 0; i < p->core.nb; ++i) {
+        proj_tactic_t &t = p->core.tactics[i];
+        while (t.kernel == PROJ_KERNEL_STREAM && t.split < 64 &&
+               tp1::stream_lds_bytes(K, t) > p->lds_limit)
+            ++t.split;
+    }
+    rc = alloc_workspace(p, tp1::plan_workspace(p->core));
+    if (rc != PROJ_OK) {
+        delete p;
+        return rc;
+    }
+    *out = p;
+    return PROJ_OK;
+}
+
+void proj_free(proj_plan_t *plan) {
+    if (!plan) return;
+    if (plan->ws && !(plan->core.flags & PROJ_PLAN_HOST_ONLY)) {
+        int cur = -1;
+        if (hipGetDevice(&cur) == hipSuccess && cur != plan->device)
+            (void)hipSetDevice(plan->device);
+        (void)hipFree(plan->ws);
+        if (cur >= 0 && cur != plan->device) (void)hipSetDevice(cur);
+    }
+    delete plan;
+}
+
+int proj_plan_tactic(const proj_plan_t *plan, int B, proj_tactic_t *tactic,
+                     int *bin) {
+    if (!plan || !tactic) return PROJ_EINVAL;
+    const int i = tp1::bin_index(plan->core, B);
+    if (i < 0) return PROJ_EBATCH;
+    *tactic = plan->core.tactics[i];
+    if (bin) *bin = plan->core.batches[i];
+    return PROJ_OK;
+}
+
+int proj_plan_set_tactic(proj_plan_t *plan, int bin, const proj_tactic_t *tactic) {
+    if (!plan || !tactic) return PROJ_EINVAL;
+    int i = -1;
+    for (int j = 0; j < plan->core.nb; ++j)
+        if (plan->core.batches[j] == bin) i = j;
+    if (i < 0) return PROJ_EINVAL;
+    if (tp1::check_tactic(plan->core.N, plan->core.K, bin, *tactic) != PROJ_OK)
+        return PROJ_EINVAL;
+    if (tactic->kernel == PROJ_KERNEL_STREAM &&
+        tp1::stream_lds_bytes(plan->core.K, *tactic) > plan->lds_limit)
+        return PROJ_EINVAL;
+    const int rc = alloc_workspace(plan, tp1::tactic_workspace(plan->core.N, plan->core.K, *tactic));
+    if (rc != PROJ_OK) return rc;
+    plan->core.tactics[i] = *tactic;
+    return PROJ_OK;
+}
+
+int proj_plan_kernel_name(const proj_plan_t *plan, int B, char *buf, size_t len) {
+    if (!plan || !buf || len == 0) return PROJ_EINVAL;
+    const int i = tp1::bin_index(plan->core, B);
+    if (i < 0) return PROJ_EBATCH;
+    return tp1::kernel_name(plan->core.K, plan->core.tactics[i], buf, len) == 0
+               ? PROJ_OK
+               : PROJ_EINVAL;
+}
+
+size_t proj_plan_workspace_bytes(const proj_plan_t *plan) {
+    return plan ? plan->ws_bytes : 0;
+}
+
+int proj_run(const proj_plan_t *plan, int B, const void *x, long ldx, const void *W,
+             void *y, void *stream) {
+    if (!plan) return PROJ_EINVAL;
+    const tp1::PlanCore &c = plan->core;
+    if (B < 0 || B > c.batches[c.nb - 1]) return PROJ_EBATCH;
+    if (ldx == 0) ldx = c.K;
+    if (ldx < c.K) return PROJ_EINVAL;
+    if (B == 0) return PROJ_OK;
+    if (!x || !W || !y) return PROJ_EINVAL;
+    if (!aligned16(x) || !aligned16(W) || !aligned16(y) || (ldx % 8) != 0)
+        return PROJ_EALIGN;
+    // y must not overlap x or W (byte ranges).
+    const uintptr_t yb = reinterpret_cast<uintptr_t>(y);
+    const uintptr_t ye = yb + (uintptr_t)B * c.N * 2u;
+    const uintptr_t xb = reinterpret_cast<uintptr_t>(x);
+    const uintptr_t xe = xb + ((uintptr_t)(B - 1) * ldx + c.K) * 2u;
+    const uintptr_t wb = reinterpret_cast<uintptr_t>(W);
+    const uintptr_t we = wb + (uintptr_t)c.N * c.K * 2u;
+    if ((yb < xe && xb < ye) || (yb < we && wb < ye)) return PROJ_EINVAL;
+    if (c.flags & PROJ_PLAN_HOST_ONLY) return PROJ_ENODEV;
+    const int i = tp1::bin_index(c, B);
+    if (i < 0) return PROJ_EBATCH;
+    const proj_tactic_t &t = c.tactics[i];
+    if (tp1::tactic_workspace(c.N, c.K, t) > plan->ws_bytes) return PROJ_EINVAL;
+    tp1::LaunchShape sh{c.N,
+                        c.K,
+                        B,
+                        static_cast<const uint16_t *>(x),
+                        ldx,
+                        static_cast<const uint16_t *>(W),
+                        static_cast<uint16_t *>(y),
+                        static_cast<float *>(plan->ws),
+                        c.num_cus};
+    const hipError_t e = tp1::launch_projection(sh, t, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return PROJ_EHIP;
+    return PROJ_OK;
+}
+
+int proj_run_layers(const proj_plan_t *in, const proj_plan_t *out, int L, int B,
+                    const void *x0, long ldx0, const void *const *W_in,
+                    const void *const *W_o, void *y_in, void *y_o, void *stream) {
+    if (!in || !out || L < 0 || !W_in || !W_o) return PROJ_EINVAL;
+    const tp1::PlanCore &a = in->core;
+    const tp1::PlanCore &b = out->core;
+    if (b.N != a.K || b.K > a.N) return PROJ_EINVAL;
+    if (B < 0 || B > a.batches[a.nb - 1] || B > b.batches[b.nb - 1]) return PROJ_EBATCH;
+    if (L == 0 || B == 0) return PROJ_OK;
+    if (!x0 || !y_in || !y_o) return PROJ_EINVAL;
+    for (int l = 0; l < L; ++l)
+        if (!W_in[l] || !W_o[l]) return PROJ_EINVAL;
+    const size_t in_stride = (size_t)B * a.N * 2u;   // bytes per layer
+    const size_t o_stride = (size_t)B * b.N * 2u;
+    const void *x = x0;
+    long ldx = ldx0;
+    for (int l = 0; l < L; ++l) {
+        char *yi = static_cast<char *>(y_in) + l * in_stride;
+        char *yo = static_cast<char *>(y_o) + l * o_stride;
+        int rc = proj_run(in, B, x, ldx, W_in[l], yi, stream);
+        if (rc != PROJ_OK) return rc;
+        rc = proj_run(out, B, yi, a.N, W_o[l], yo, stream);
+        if (rc != PROJ_OK) return rc;
+        x = yo;
+        ldx = b.N;
+    }
+    return PROJ_OK;
+}
+
+int proj_read_probe(const void *buf, size_t bytes, float *sink, int waves_per_cu,
+                    void *stream) {
+    if (!buf || !sink || bytes == 0 || (bytes % 16) != 0) return PROJ_EINVAL;
+    if (!aligned16(buf)) return PROJ_EALIGN;
+    if (waves_per_cu < 0 || waves_per_cu > 32) return PROJ_EINVAL;
+    int dev = -1, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        return PROJ_EHIP;
+    const hipError_t e = tp1::launch_read_probe(buf, bytes, sink, waves_per_cu, cus,
+                                                static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PROJ_OK : PROJ_EHIP;
+}
+
+}  // extern "C"

@@ -1,0 +1,150 @@
+"""Tactic measurement: time candidate tactics per (N, K, batch bin) on the GPU
+and pick the table the library ships (tactics_table.cpp).
+
+The vLLM dep page keeps a per-batch tactic table for its projections (opening
+text: "per batch (DEP_PROJECTION)", "per batch (DEP_OPROJ)"; section
+"_bins"); this tool builds the MI355X one by measurement.  Each candidate is
+timed over rotated weight copies (>= 1 GB, so every call streams its weight
+from HBM), median of `reps` calls; ties within 1% go to fewer launches (no
+split-K pass), then the smaller split, then fewer rows per wave.  The
+crossover is the smallest batch whose best tactic is an MFMA one.
+
+    python -m tp1_skinny_bf16_amd.tune --shape 14560x7168 --bins 1,2,4 --out t.json
+"""
+from __future__ import annotations
+
+import argparse
+import itertools
+import json
+import sys
+import time
+
+import torch
+
+from . import KERNEL_MFMA, KERNEL_STREAM, Plan, ProjError, Tactic
+from .timing import gbs, rotation_copies, time_calls
+
+SHAPES = {"dsa": (14560, 7168), "oproj": (7168, 12288), "kda": (49376, 7168)}
+
+
+def next_pow2(v: int) -> int:
+    p = 1
+    while p < v:
+        p <<= 1
+    return p
+
+
+def candidates(bin_: int, full: bool = False):
+    out = []
+    if bin_ <= 8:
+        bc = next_pow2(bin_)
+        for rows, split, waves, wpc in itertools.product(
+                (1, 2, 4), (1, 2, 3, 4), (1, 2, 4, 8), (2, 4, 6, 8, 12, 16)):
+            if not full and waves == 8 and wpc < 8:
+                continue
+            out.append(Tactic(KERNEL_STREAM, bc, split, rows, waves, wpc))
+    if bin_ >= 2:
+        bc = max(16, next_pow2(bin_))
+        for rows, split, waves, wpc in itertools.product(
+                (1, 2, 4), (1, 2, 3, 4, 6), (1, 2, 4), (0, 2, 4, 8)):
+            if bc == 256 and rows > 1:
+                continue
+            out.append(Tactic(KERNEL_MFMA, bc, split, rows, waves, wpc))
+    return out
+
+
+def _key(res):
+    t = res["tactic"]
+    return (res["us"], t["split"] > 1, t["split"], t["rows"])
+
+
+def measure(N: int, K: int, bins, reps: int = 40, log=None, full: bool = False):
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    W0 = (torch.randn((N, K), generator=g, device=dev) * 0.02).to(torch.bfloat16)
+    copies = rotation_copies(W0)
+    bmax = max(bins)
+    x = torch.randn((bmax, K), generator=g, device=dev).to(torch.bfloat16)
+    plan = Plan(N, K, bins)
+    result = {"N": N, "K": K, "copies": len(copies), "bins": {}}
+    for b in bins:
+        y = torch.empty((b, N), dtype=torch.bfloat16, device=dev)
+        xb = x[:b]
+        st = torch.cuda.current_stream().cuda_stream
+        rows = []
+        for t in candidates(b, full):
+            try:
+                plan.set_tactic(b, t)
+            except ProjError:
+                continue
+            calls = [(lambda W=W: plan.run_ptr(b, xb.data_ptr(), K, W.data_ptr(),
+                                               y.data_ptr(), st)) for W in copies]
+            r = time_calls(calls, warmup=2, reps=reps)
+            rows.append({"tactic": t.as_dict(), "us": round(r["us_median"], 2),
+                         "kernel": plan.kernel_name(b)})
+        rows.sort(key=_key)
+        best = rows[0]
+        # ties within 1%: prefer no split pass, then smaller split, fewer rows
+        near = [r for r in rows if r["us"] <= best["us"] * 1.01]
+        near.sort(key=lambda r: (r["tactic"]["split"] > 1, r["tactic"]["split"],
+                                 r["tactic"]["rows"], r["us"]))
+        chosen = near[0]
+        nbytes = 2 * N * K + 2 * b * K + 2 * b * N
+        result["bins"][b] = {"chosen": chosen, "GBps": round(gbs(nbytes, chosen["us"]), 1),
+                             "top": rows[:8], "n_candidates": len(rows)}
+        best_stream = min((r for r in rows if r["tactic"]["kernel"] == "stream"),
+                          key=lambda r: r["us"], default=None)
+        best_mfma = min((r for r in rows if r["tactic"]["kernel"] == "mfma"),
+                        key=lambda r: r["us"], default=None)
+        result["bins"][b]["best_stream_us"] = best_stream["us"] if best_stream else None
+        result["bins"][b]["best_mfma_us"] = best_mfma["us"] if best_mfma else None
+        if log:
+            log(f"{N}x{K} B={b}: {chosen['us']:.2f} us {result['bins'][b]['GBps']} GB/s "
+                f"{chosen['kernel']} {chosen['tactic']} (stream {result['bins'][b]['best_stream_us']}"
+                f" / mfma {result['bins'][b]['best_mfma_us']}, {len(rows)} candidates)")
+        plan.set_tactic(b, Tactic(**{**chosen["tactic"],
+                                     "kernel": KERNEL_STREAM if chosen["tactic"]["kernel"] == "stream"
+                                     else KERNEL_MFMA}))
+    mfma_bins = [b for b in bins if result["bins"][b]["chosen"]["tactic"]["kernel"] == "mfma"]
+    result["crossover"] = min(mfma_bins) if mfma_bins else None
+    return result
+
+
+def table_rows(result) -> str:
+    lines = []
+    for b, r in result["bins"].items():
+        t = r["chosen"]["tactic"]
+        k = "PROJ_KERNEL_STREAM" if t["kernel"] == "stream" else "PROJ_KERNEL_MFMA"
+        lines.append(f"    {{{result['N']}, {result['K']}, {b}, {{{k}, {t['bcap']}, {t['split']}, "
+                     f"{t['rows']}, {t['waves']}, {t['wpc']}}}}},  // {r['chosen']['us']} us, "
+                     f"{r['GBps']} GB/s")
+    return "\n".join(lines)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--shape", action="append", required=True,
+                    help="NxK or one of " + ",".join(SHAPES))
+    ap.add_argument("--bins", default="1,2,4,8,16,32,64,128,256")
+    ap.add_argument("--reps", type=int, default=40)
+    ap.add_argument("--full", action="store_true")
+    ap.add_argument("--out", required=True)
+    a = ap.parse_args()
+    bins = [int(v) for v in a.bins.split(",")]
+    allres = []
+    t0 = time.time()
+    for sh in a.shape:
+        N, K = SHAPES[sh] if sh in SHAPES else (int(v) for v in sh.split("x"))
+        res = measure(N, K, bins, a.reps, log=lambda m: print(m, flush=True), full=a.full)
+        allres.append(res)
+        print(table_rows(res), flush=True)
+        print(f"crossover (first MFMA bin) for {N}x{K}: {res['crossover']}  "
+              f"[{time.time() - t0:.0f} s]", flush=True)
+        with open(a.out, "w") as f:
+            json.dump(allres, f, indent=1)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

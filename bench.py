@@ -37,7 +37,22 @@ def _args():
     ap.add_argument("--report", default=None, help="write the all-config report here")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 256 MiB device copy 5 times, the known-size "
+                         "reference that scales FETCH_SIZE / WRITE_SIZE counters")
     return ap.parse_args()
+
+
+def copy_calibration(torch):
+    """A plain device-to-device copy of 256 MiB: reads and writes exactly
+    268435456 bytes, so profiler byte counters can be scaled by it."""
+    n = 256 * 1024 * 1024 // 2
+    src = torch.ones(n, dtype=torch.bfloat16, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    _say("copy calibration: 5 x 268435456-byte device copies done")
 
 
 def _say(*a):
@@ -71,16 +86,18 @@ def headline(args, torch, tp, wl, timing):
 
     for s in range(args.warmup):
         step(s)
-    # per-call HIP events on the launch stream, over the timed region
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in cfg.batches] for _ in range(args.steps)]
+    # Timed region: the K steps' calls, grouped by batch size (B-major) so that
+    # each size's K calls run back to back between one pair of HIP events on
+    # the launch stream; a step is still one call per batch size.
+    ev = {B: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for B in cfg.batches}
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(args.steps):
-        for j, B in enumerate(cfg.batches):
-            ev[s][j][0].record(stream)
+    for j, B in enumerate(cfg.batches):
+        ev[B][0].record(stream)
+        for s in range(args.steps):
             call(s * nb + j, B)
-            ev[s][j][1].record(stream)
+        ev[B][1].record(stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / args.steps
@@ -89,8 +106,7 @@ def headline(args, torch, tp, wl, timing):
 
     per_b = {}
     for j, B in enumerate(cfg.batches):
-        us = [ev[s][j][0].elapsed_time(ev[s][j][1]) * 1e3 for s in range(args.steps)]
-        mean = sum(us) / len(us)
+        mean = ev[B][0].elapsed_time(ev[B][1]) * 1e3 / args.steps
         tac, _ = plan.tactic(B)
         per_b[B] = {"us_per_call": round(mean, 2),
                     "GBps": round(timing.gbs(wl.algorithmic_bytes(B, cfg.N, cfg.K), mean), 1),
@@ -108,12 +124,29 @@ def headline(args, torch, tp, wl, timing):
     achieved = timing.gbs(bytes_per_launch, avg_us)
     roof = {"bound": "hbm", "kernel": name, "achieved": round(achieved, 1),
             "peak": timing.HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / timing.HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round(achieved / timing.HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(name),
             "avg_launch_us": round(avg_us, 2), "bytes_per_launch": int(bytes_per_launch)}
     res = {"cfg": cfg, "t": t, "plan": plan, "value": value, "ms": ms_per_step,
            "per_b": per_b, "roofline": roof, "step_bytes": step_bytes,
            "copies": ncopy}
     return res
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary
+    (profiles/traffic.json), or None when it was taken from another version
+    of the kernel source or never taken."""
+    from tp1_skinny_bf16_amd import profile_summary
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    if data.get("source_hash") != profile_summary.source_hash():
+        return None
+    entry = data.get("kernels", {}).get(kernel.split("+")[0])
+    return int(entry["traffic"]) if entry else None
 
 
 def cpu_baseline(args, cfg, t, wl):
@@ -231,6 +264,8 @@ def main():
         cpu = cpu_baseline(args, h["cfg"], h["t"], wl)
     if args.report:
         report(args, torch, tp, wl, timing)
+    if args.copy_calibration:
+        copy_calibration(torch)
     cfg = h["cfg"]
     line = {
         "metric": "achieved HBM GB/s (algorithmic W+x+y bytes / time), TP1 BF16 decode "

@@ -48,7 +48,13 @@ enum proj_status {
 enum proj_kernel {
     PROJ_KERNEL_STREAM = 1, /* split-K weight stream: VALU dot products,
                                lanes along K, wavefront reductions         */
-    PROJ_KERNEL_MFMA = 2    /* BF16 MFMA tiles (16x16x32), FP32 accumulate */
+    PROJ_KERNEL_MFMA = 2,   /* BF16 MFMA tiles (16x16x32), FP32 accumulate */
+    PROJ_KERNEL_STREAM_DOT2 = 3, /* the weight stream with v_dot2 BF16 pair
+                               products: FP32 accumulation whose additions
+                               are not always IEEE round-to-nearest      */
+    PROJ_KERNEL_MFMA_LDS = 4 /* MFMA tiles fed from a per-wave LDS tile that
+                               the weight reaches with 1 KB row loads
+                               (bcap 16 or 32, rows 1 or 2)              */
 };
 
 /* Plan flags. */
@@ -70,7 +76,8 @@ enum proj_kernel {
  *   split  : number of K slices S; S > 1 adds a fixed-order reduction pass
  *   rows   : STREAM: W rows a wave carries per pass (1, 2 or 4)
  *            MFMA:   16-column N tiles per wave (1, 2 or 4; 1 at bcap 256)
- *   waves  : waves per workgroup (STREAM 1..8, MFMA 1..4)
+ *   waves  : waves per workgroup (STREAM 1..8, MFMA 1..4, and MFMA partial
+ *            tiles must fit the LDS: waves * 2 * bcap/16 * rows KB <= 160)
  *   wpc    : STREAM: waves per compute unit the grid is sized for
  *            MFMA:   0 = one wave per N range (grid from N), else as STREAM
  */

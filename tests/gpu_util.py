@@ -93,6 +93,15 @@ def candidate_tactics(N: int, K: int, bin_: int):
                 for split in (1, 3):
                     for waves, wpc in ((4, 8), (2, 4), (8, 16), (1, 1), (3, 5)):
                         out.append(tp.Tactic(tp.KERNEL_STREAM, bc, split, rows, waves, wpc))
+                    out.append(tp.Tactic(tp.KERNEL_STREAM_DOT2, bc, split, rows, 4, 8))
+    if bin_ <= 32:
+        for bc in (16, 32):
+            if bc < bin_:
+                continue
+            for rows in (1, 2):
+                for split in (1, 2):
+                    for waves, wpc in ((4, 0), (2, 3), (1, 8), (3, 4)):
+                        out.append(tp.Tactic(tp.KERNEL_MFMA_LDS, bc, split, rows, waves, wpc))
     for bc in (16, 32, 64, 128, 256):
         if bc < bin_:
             continue
@@ -100,6 +109,6 @@ def candidate_tactics(N: int, K: int, bin_: int):
             if bc == 256 and rows > 1:
                 continue
             for split in (1, 2):
-                for wpc in (0, 3):
-                    out.append(tp.Tactic(tp.KERNEL_MFMA, bc, split, rows, 4, wpc))
+                for waves, wpc in ((4, 0), (2, 3), (1, 8), (3, 4)):
+                    out.append(tp.Tactic(tp.KERNEL_MFMA, bc, split, rows, waves, wpc))
     return out

@@ -93,7 +93,7 @@ def test_every_planned_bin_gets_a_valid_tactic(N, K):
     for b in range(1, 257):
         t, bin_ = p.tactic(b)
         assert bin_ >= b and t.bcap >= bin_
-        assert t.kernel in (tp.KERNEL_STREAM, tp.KERNEL_MFMA)
+        assert t.kernel in tp.KERNEL_NAMES
         # setting the chosen tactic back must validate
         p.set_tactic(bin_, t)
 

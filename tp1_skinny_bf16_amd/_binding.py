@@ -24,7 +24,11 @@ PROJ_ENODEV = -6
 
 KERNEL_STREAM = 1
 KERNEL_MFMA = 2
-KERNEL_NAMES = {KERNEL_STREAM: "stream", KERNEL_MFMA: "mfma"}
+KERNEL_STREAM_DOT2 = 3
+KERNEL_MFMA_LDS = 4
+KERNEL_NAMES = {KERNEL_STREAM: "stream", KERNEL_MFMA: "mfma", KERNEL_STREAM_DOT2: "stream_dot2",
+                KERNEL_MFMA_LDS: "mfma_lds"}
+KERNEL_IDS = {v: k for k, v in KERNEL_NAMES.items()}
 
 PLAN_HOST_ONLY = 0x1
 MAX_BATCH = 256

@@ -32,6 +32,7 @@
 namespace tp1 {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -42,6 +43,15 @@ __device__ __forceinline__ u32x4 load_stream(const uint16_t *p) {
 }
 __device__ __forceinline__ u32x4 load_cached(const uint16_t *p) {
     return *reinterpret_cast<const u32x4 *>(p);
+}
+
+// BF16 pair dot product into FP32 (v_dot2c_f32_bf16).  Measured on gfx950:
+// the products are exact but the three-term addition is not always IEEE
+// round-to-nearest (it can differ from it by a few FP32 ulps, and not
+// symmetrically in sign), so this arithmetic is a separate tactic.
+__device__ __forceinline__ float dot2(unsigned a, unsigned b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                           __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
 // FP32 -> BF16, round to nearest, ties to even; NaN -> canonical quiet NaN.
@@ -117,7 +127,7 @@ __device__ __forceinline__ int wave_of_step(int q, int T, int NW) {
     return (int)(((long)(q + 1) * NW + T - 1) / T) - 1;
 }
 
-template <int BC, int R, int P>
+template <int BC, int R, int P, bool D2>
 __global__ __launch_bounds__(512) void stream_kernel(StreamArgs a) {
     extern __shared__ __align__(16) uint16_t xs[];
     __shared__ float part[kStreamMaxWaves][2][R * BC];  // [wave][head/tail][r*BC+b]
@@ -204,6 +214,18 @@ __global__ __launch_bounds__(512) void stream_kernel(StreamArgs a) {
 #pragma unroll
                     for (int b = 0; b < BC; ++b) {
                         const u32x4 xv = *reinterpret_cast<const u32x4 *>(xs + b * a.ksp + kk);
+                        if constexpr (D2) {
+#pragma unroll
+                            for (int r = 0; r < R; ++r) {
+                                float t = acc[r][b];
+                                t = dot2(w[r].x, xv.x, t);
+                                t = dot2(w[r].y, xv.y, t);
+                                t = dot2(w[r].z, xv.z, t);
+                                t = dot2(w[r].w, xv.w, t);
+                                acc[r][b] = t;
+                            }
+                            continue;
+                        }
                         const float x0 = bf_lo(xv.x), x1 = bf_hi(xv.x), x2 = bf_lo(xv.y),
                                     x3 = bf_hi(xv.y), x4 = bf_lo(xv.z), x5 = bf_hi(xv.z),
                                     x6 = bf_lo(xv.w), x7 = bf_hi(xv.w);
@@ -288,11 +310,19 @@ __global__ __launch_bounds__(512) void stream_kernel(StreamArgs a) {
 // the A operand and column (l % 16) of the B operand, each with 8 K values
 // of K group (l / 16); the accumulator lane l holds rows 4*(l/16) + 0..3 of
 // column l % 16.  The K order inside a group only permutes the sum, so each
-// lane simply loads 8 consecutive K of its row.  x is the A operand (batch
-// rows), W the B operand (output columns); a wave owns a contiguous range of
-// 16*NT-column units and walks K in 32-wide steps with a ring of P steps of
-// unconditional loads in flight (rows past B or N are clamped onto valid
-// data and their results discarded).
+// lane simply loads 8 consecutive K of its row.  x is the A operand (MT
+// tiles of 16 batch rows), W the B operand (NT tiles of 16 output columns).
+//
+// Work is split as in the stream kernel: workgroup g owns rows
+// [N*g/G, N*(g+1)/G) for one K slice, cut into groups of 16*NT rows; the
+// (group, 32-wide K step) sequence is split evenly over the waves, each
+// wave a contiguous run.  A group a wave covers entirely is written out; a
+// group cut by a wave boundary leaves per-wave partial tiles in LDS that
+// are added in wave order after one barrier.  W loads here are ordinary
+// cached loads: each instruction reads 64 B of each of 16 rows, and the
+// other half of every 128 B line is read by the next step, so keeping the
+// line in cache pays.  Rows past B or past the workgroup's rows are clamped
+// onto valid data and their results discarded.
 // ---------------------------------------------------------------------------
 struct MfmaArgs {
     const uint16_t *x;
@@ -302,23 +332,27 @@ struct MfmaArgs {
     float *ws;
     int N, K, B;
     int ks;    // K elements per slice (multiple of 32)
-    int upw;   // N units (16*NT columns) per wave
     int S;
 };
 
 template <int MT, int NT, int P>
 __global__ __launch_bounds__(256) void mfma_kernel(MfmaArgs a) {
+    extern __shared__ __align__(16) float mpart[];  // [wave][2][MT*NT][64][4]
     const int lane = threadIdx.x & 63;
-    const int gw = blockIdx.x * uniform(blockDim.x >> 6) + uniform(threadIdx.x >> 6);
+    const int NW = uniform(blockDim.x >> 6);
+    const int wave = uniform(threadIdx.x >> 6);
     const int s = blockIdx.y;
     const int k0 = s * a.ks;
     const int klen = min(a.K - k0, a.ks);
-    const int U = (a.N + 16 * NT - 1) / (16 * NT);
-    const int u_begin = gw * a.upw;
-    const int u_end = min(U, u_begin + a.upw);
-    if (u_begin >= u_end) return;
-    const int C = (klen + 31) >> 5;
-    const int T = (u_end - u_begin) * C;
+    const int row0 = (int)((long)a.N * blockIdx.x / gridDim.x);
+    const int rows = (int)((long)a.N * (blockIdx.x + 1) / gridDim.x) - row0;
+    constexpr int GR = 16 * NT;                // rows (output columns) per group
+    const int C = (klen + 31) >> 5;            // 32-wide K steps per group
+    const int Gb = (rows + GR - 1) / GR;
+    const int Tb = Gb * C;
+    const int q0 = (int)((long)Tb * wave / NW);
+    const int q1 = (int)((long)Tb * (wave + 1) / NW);
+    const int T = q1 - q0;
     const bool ragged = (klen & 31) != 0;
     const int lrow = lane & 15, lgrp = lane >> 4;
 
@@ -326,80 +360,308 @@ __global__ __launch_bounds__(256) void mfma_kernel(MfmaArgs a) {
 #pragma unroll
     for (int m = 0; m < MT; ++m)
         xrow[m] = a.x + (size_t)min(m * 16 + lrow, a.B - 1) * a.ldx + k0;
-    const uint16_t *wslice = a.W + k0;
+    const uint16_t *wblk = a.W + (size_t)row0 * a.K + k0;
+    float *mine_part = mpart + (size_t)wave * 2 * MT * NT * 256;
 
-    u32x4 wb[P][NT];
-    u32x4 xb[P][MT];
-    f32x4 acc[MT][NT];
-#pragma unroll
-    for (int m = 0; m < MT; ++m)
-#pragma unroll
-        for (int n = 0; n < NT; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    int lt = 0, lu = u_begin, lc = 0;
-    auto load_step = [&](u32x4 (&w)[NT], u32x4 (&xx)[MT]) {
-        const int kk = min(lc * 32 + lgrp * 8, klen - 8);
-#pragma unroll
-        for (int n = 0; n < NT; ++n) {
-            const int col = min(lu * 16 * NT + n * 16 + lrow, a.N - 1);
-            w[n] = load_stream(wslice + (size_t)col * a.K + kk);
-        }
-#pragma unroll
-        for (int m = 0; m < MT; ++m) xx[m] = load_cached(xrow[m] + kk);
-        if (lt < T - 1) {
-            ++lt;
-            if (++lc == C) { lc = 0; ++lu; }
-        }
+    auto store_out = [&](int row, int col, float v) {
+        if (a.S == 1)
+            a.y[(size_t)row * a.N + col] = to_bf16(v);
+        else
+            a.ws[((size_t)s * a.B + row) * a.N + col] = v;
     };
 
+    if (T > 0) {
+        u32x4 wb[P][NT];
+        u32x4 xb[P][MT];
+        f32x4 acc[MT][NT];
 #pragma unroll
-    for (int j = 0; j < P; ++j) load_step(wb[j], xb[j]);
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int n = 0; n < NT; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    int cu = u_begin, cc = 0;
-    for (int t0 = 0; t0 < T; t0 += P) {
+        int lt = 0, lg = q0 / C, lc = q0 - (q0 / C) * C;
+        auto load_step = [&](u32x4 (&w)[NT], u32x4 (&xx)[MT]) {
+            const int kk = min(lc * 32 + lgrp * 8, klen - 8);
 #pragma unroll
-        for (int j = 0; j < P; ++j) {
-            if (t0 + j < T) {
-                u32x4 w[NT];
+            for (int n = 0; n < NT; ++n) {
+                const int r = min(lg * GR + n * 16 + lrow, rows - 1);
+                w[n] = load_cached(wblk + (size_t)r * a.K + kk);
+            }
 #pragma unroll
-                for (int n = 0; n < NT; ++n) w[n] = wb[j][n];
-                if (ragged && cc == C - 1) {
-                    const bool dead = cc * 32 + lgrp * 8 >= klen;  // past the slice
+            for (int m = 0; m < MT; ++m) xx[m] = load_cached(xrow[m] + kk);
+            if (lt < T - 1) {
+                ++lt;
+                if (++lc == C) { lc = 0; ++lg; }
+            }
+        };
+
 #pragma unroll
-                    for (int n = 0; n < NT; ++n)
-                        w[n] = dead ? u32x4{0u, 0u, 0u, 0u} : w[n];
+        for (int j = 0; j < P; ++j) load_step(wb[j], xb[j]);
+
+        int cg = q0 / C, cc = q0 - (q0 / C) * C;
+        for (int t0 = 0; t0 < T; t0 += P) {
+#pragma unroll
+            for (int j = 0; j < P; ++j) {
+                if (t0 + j < T) {
+                    u32x4 w[NT];
+#pragma unroll
+                    for (int n = 0; n < NT; ++n) w[n] = wb[j][n];
+                    if (ragged && cc == C - 1) {
+                        const bool dead = cc * 32 + lgrp * 8 >= klen;  // past the slice
+#pragma unroll
+                        for (int n = 0; n < NT; ++n)
+                            w[n] = dead ? u32x4{0u, 0u, 0u, 0u} : w[n];
+                    }
+#pragma unroll
+                    for (int m = 0; m < MT; ++m)
+#pragma unroll
+                        for (int n = 0; n < NT; ++n)
+                            acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                __builtin_bit_cast(bf16x8_t, xb[j][m]),
+                                __builtin_bit_cast(bf16x8_t, w[n]), acc[m][n], 0, 0, 0);
                 }
+                load_step(wb[j], xb[j]);
+                if (t0 + j < T) {
+                    if (cc == C - 1 || t0 + j == T - 1) {
+                        const bool started_here = cg * C >= q0;
+                        if (cc == C - 1 && started_here) {
+#pragma unroll
+                            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                                for (int n = 0; n < NT; ++n) {
+                                    const int r = cg * GR + n * 16 + lrow;
+#pragma unroll
+                                    for (int v = 0; v < 4; ++v) {
+                                        const int b = m * 16 + lgrp * 4 + v;
+                                        if (b < a.B && r < rows) store_out(b, row0 + r, acc[m][n][v]);
+                                    }
+                                }
+                        } else {
+                            float *slot = mine_part + (started_here ? 1 : 0) * MT * NT * 256;
+#pragma unroll
+                            for (int m = 0; m < MT; ++m)
+#pragma unroll
+                                for (int n = 0; n < NT; ++n)
+                                    *reinterpret_cast<f32x4 *>(slot + ((m * NT + n) * 64 + lane) * 4) =
+                                        acc[m][n];
+                        }
+#pragma unroll
+                        for (int m = 0; m < MT; ++m)
+#pragma unroll
+                            for (int n = 0; n < NT; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+                    }
+                    if (++cc == C) { cc = 0; ++cg; }
+                }
+            }
+        }
+    }
+
+    // Groups cut by a wave boundary: add the partial tiles in wave order.
+    __syncthreads();
+    constexpr int TILE = MT * NT * 256;  // floats of one partial
+    for (int i = 1; i < NW; ++i) {
+        const int qi = (int)((long)Tb * i / NW);
+        const int qp = (int)((long)Tb * (i - 1) / NW);
+        const int g = qi / C;
+        const bool split = qi < Tb && (qi - g * C) != 0;
+        const bool seen = i > 1 && qp / C == g && (qp - (qp / C) * C) != 0;
+        if (!split || seen) continue;
+        const int wlo = wave_of_step(g * C, Tb, NW);
+        const int whi = wave_of_step(g * C + C - 1, Tb, NW);
+        for (int e = threadIdx.x; e < TILE; e += blockDim.x) {
+            float sum = 0.f;
+            for (int v = wlo; v <= whi; ++v) {
+                const int qv = (int)((long)Tb * v / NW);
+                const int qv1 = (int)((long)Tb * (v + 1) / NW);
+                if (qv == qv1) continue;
+                sum += mpart[((size_t)v * 2 + (g * C < qv ? 0 : 1)) * TILE + e];
+            }
+            // e = ((m*NT + n)*64 + l)*4 + vv
+            const int vv = e & 3, l = (e >> 2) & 63, mn = e >> 8;
+            const int m = mn / NT, n = mn - (mn / NT) * NT;
+            const int r = g * GR + n * 16 + (l & 15);
+            const int b = m * 16 + (l >> 4) * 4 + vv;
+            if (b < a.B && r < rows) store_out(b, row0 + r, sum);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// LDS-transposed MFMA kernel (mid batches).
+// The weight is read exactly as in the stream kernel -- lanes along K, each
+// load 1 KB of one row -- for a group of 16*NT rows and a 512-wide K chunk,
+// then written to a padded per-wave LDS tile and read back in MFMA B-operand
+// layout (lane (n, g) reads row n, K 32j + 8g..+7 of the chunk; the 1040-byte
+// row pitch puts the 16 rows of a read in distinct banks).  x (the A
+// operand, MT tiles of 16 batch rows) is read with ordinary cached loads,
+// one chunk ahead.  Work split, partial-tile combine and clamping are as in
+// mfma_kernel; a step here is one (group, chunk).
+// ---------------------------------------------------------------------------
+constexpr int kTilePitch = 520;  // bf16 elements per LDS tile row (1040 B)
+
+template <int MT, int NT>
+__global__ __launch_bounds__(256) void mfma_lds_kernel(MfmaArgs a) {
+    extern __shared__ __align__(16) float tl_lds[];
+    constexpr int GR = 16 * NT;
+    const int lane = threadIdx.x & 63;
+    const int NW = uniform(blockDim.x >> 6);
+    const int wave = uniform(threadIdx.x >> 6);
+    const int s = blockIdx.y;
+    const int k0 = s * a.ks;
+    const int klen = min(a.K - k0, a.ks);
+    const int row0 = (int)((long)a.N * blockIdx.x / gridDim.x);
+    const int rows = (int)((long)a.N * (blockIdx.x + 1) / gridDim.x) - row0;
+    const int C = (klen + 511) >> 9;           // 512-wide chunks per group
+    const int Gb = (rows + GR - 1) / GR;
+    const int Tb = Gb * C;
+    const int q0 = (int)((long)Tb * wave / NW);
+    const int q1 = (int)((long)Tb * (wave + 1) / NW);
+    const int T = q1 - q0;
+    const bool ragged = (klen & 511) != 0;
+    const int lrow = lane & 15, lgrp = lane >> 4;
+    const int lk = lane * 8;
+
+    // LDS: per-wave tiles, then per-wave partial slots.
+    uint16_t *tile = reinterpret_cast<uint16_t *>(tl_lds) + (size_t)wave * GR * kTilePitch;
+    float *parts = tl_lds + (size_t)NW * GR * kTilePitch / 2;
+    constexpr int TILE = MT * NT * 256;  // floats of one partial
+    float *mine_part = parts + (size_t)wave * 2 * TILE;
+
+    const uint16_t *xrow[MT];
+#pragma unroll
+    for (int m = 0; m < MT; ++m)
+        xrow[m] = a.x + (size_t)min(m * 16 + lrow, a.B - 1) * a.ldx + k0 + lgrp * 8;
+    const uint16_t *wblk = a.W + (size_t)row0 * a.K + k0;
+
+    auto store_out = [&](int row, int col, float v) {
+        if (a.S == 1)
+            a.y[(size_t)row * a.N + col] = to_bf16(v);
+        else
+            a.ws[((size_t)s * a.B + row) * a.N + col] = v;
+    };
+
+    if (T > 0) {
+        u32x4 wr[GR];        // this step's weight rows (lanes along K)
+        u32x4 xr[16][MT];    // this step's A fragments, 16 K steps of 32
+        f32x4 acc[MT][NT];
+#pragma unroll
+        for (int m = 0; m < MT; ++m)
+#pragma unroll
+            for (int n = 0; n < NT; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        int lt = 0, lg = q0 / C, lc = q0 - (q0 / C) * C;
+        auto load_w = [&]() {
+            const int kk = min(lc * 512 + lk, klen - 8);
+#pragma unroll
+            for (int r = 0; r < GR; ++r) {
+                const int row = min(lg * GR + r, rows - 1);
+                wr[r] = load_stream(wblk + (size_t)row * a.K + kk);
+            }
+        };
+        auto load_x = [&](int j) {
+            const int kk = min(lc * 512 + j * 32, klen - 8 - lgrp * 8);
+#pragma unroll
+            for (int m = 0; m < MT; ++m) xr[j][m] = load_cached(xrow[m] + kk);
+        };
+        auto advance = [&]() {
+            if (lt < T - 1) {
+                ++lt;
+                if (++lc == C) { lc = 0; ++lg; }
+            }
+        };
+        load_w();
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < 16; ++j) load_x(j);
+        __builtin_amdgcn_sched_barrier(0);
+        advance();
+
+        int cg = q0 / C, cc = q0 - (q0 / C) * C;
+        for (int t = 0; t < T; ++t) {
+            // Weight rows of this step -> LDS tile (zeroed past the slice).
+            const bool dead = ragged && cc == C - 1 && cc * 512 + lk >= klen;
+#pragma unroll
+            for (int r = 0; r < GR; ++r)
+                *reinterpret_cast<u32x4 *>(tile + r * kTilePitch + lk) =
+                    dead ? u32x4{0u, 0u, 0u, 0u} : wr[r];
+            // Keep the issue order: this step's tile writes, then the next
+            // step's weight loads, then the A-fragment loads (which are
+            // younger, so waiting for the weight never drains them).
+            __builtin_amdgcn_sched_barrier(0);
+            load_w();  // next step's rows go out while this one computes
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                u32x4 bfr[NT];
+#pragma unroll
+                for (int n = 0; n < NT; ++n)
+                    bfr[n] = *reinterpret_cast<const u32x4 *>(
+                        tile + (n * 16 + lrow) * kTilePitch + j * 32 + lgrp * 8);
 #pragma unroll
                 for (int m = 0; m < MT; ++m)
 #pragma unroll
                     for (int n = 0; n < NT; ++n)
                         acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8_t, xb[j][m]),
-                            __builtin_bit_cast(bf16x8_t, w[n]), acc[m][n], 0, 0, 0);
+                            __builtin_bit_cast(bf16x8_t, xr[j][m]),
+                            __builtin_bit_cast(bf16x8_t, bfr[n]), acc[m][n], 0, 0, 0);
+                load_x(j);  // this K step's A fragment for the next step
             }
-            load_step(wb[j], xb[j]);
-            if (t0 + j < T) {
-                if (cc == C - 1) {
+            advance();
+            if (cc == C - 1 || t == T - 1) {
+                const bool started_here = cg * C >= q0;
+                if (cc == C - 1 && started_here) {
 #pragma unroll
                     for (int m = 0; m < MT; ++m)
 #pragma unroll
                         for (int n = 0; n < NT; ++n) {
-                            const int col = cu * 16 * NT + n * 16 + lrow;
+                            const int r = cg * GR + n * 16 + lrow;
 #pragma unroll
                             for (int v = 0; v < 4; ++v) {
-                                const int row = m * 16 + lgrp * 4 + v;
-                                if (row < a.B && col < a.N) {
-                                    if (a.S == 1)
-                                        a.y[(size_t)row * a.N + col] = to_bf16(acc[m][n][v]);
-                                    else
-                                        a.ws[((size_t)s * a.B + row) * a.N + col] = acc[m][n][v];
-                                }
+                                const int b = m * 16 + lgrp * 4 + v;
+                                if (b < a.B && r < rows) store_out(b, row0 + r, acc[m][n][v]);
                             }
-                            acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
                         }
+                } else {
+                    float *slot = mine_part + (started_here ? 1 : 0) * TILE;
+#pragma unroll
+                    for (int m = 0; m < MT; ++m)
+#pragma unroll
+                        for (int n = 0; n < NT; ++n)
+                            *reinterpret_cast<f32x4 *>(slot + ((m * NT + n) * 64 + lane) * 4) =
+                                acc[m][n];
                 }
-                if (++cc == C) { cc = 0; ++cu; }
+#pragma unroll
+                for (int m = 0; m < MT; ++m)
+#pragma unroll
+                    for (int n = 0; n < NT; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
             }
+            if (++cc == C) { cc = 0; ++cg; }
+        }
+    }
+
+    __syncthreads();
+    for (int i = 1; i < NW; ++i) {
+        const int qi = (int)((long)Tb * i / NW);
+        const int qp = (int)((long)Tb * (i - 1) / NW);
+        const int g = qi / C;
+        const bool split = qi < Tb && (qi - g * C) != 0;
+        const bool seen = i > 1 && qp / C == g && (qp - (qp / C) * C) != 0;
+        if (!split || seen) continue;
+        const int wlo = wave_of_step(g * C, Tb, NW);
+        const int whi = wave_of_step(g * C + C - 1, Tb, NW);
+        for (int e = threadIdx.x; e < TILE; e += blockDim.x) {
+            float sum = 0.f;
+            for (int v = wlo; v <= whi; ++v) {
+                const int qv = (int)((long)Tb * v / NW);
+                const int qv1 = (int)((long)Tb * (v + 1) / NW);
+                if (qv == qv1) continue;
+                sum += parts[((size_t)v * 2 + (g * C < qv ? 0 : 1)) * TILE + e];
+            }
+            const int vv = e & 3, l = (e >> 2) & 63, mn = e >> 8;
+            const int m = mn / NT, n = mn - (mn / NT) * NT;
+            const int r = g * GR + n * 16 + (l & 15);
+            const int b = m * 16 + (l >> 4) * 4 + vv;
+            if (b < a.B && r < rows) store_out(b, row0 + r, sum);
         }
     }
 }
@@ -460,7 +722,7 @@ constexpr int mfma_ring(int MT, int NT) {
     return MT + NT <= 2 ? 8 : (MT + NT <= 3 ? 6 : (MT + NT <= 5 ? 4 : (MT + NT <= 8 ? 2 : 1)));
 }
 
-template <int BC, int R>
+template <int BC, int R, bool D2>
 hipError_t launch_stream_inst(const LaunchShape &sh, const proj_tactic_t &t,
                               hipStream_t stream) {
     constexpr int P = stream_ring(BC, R);
@@ -479,13 +741,13 @@ hipError_t launch_stream_inst(const LaunchShape &sh, const proj_tactic_t &t,
     static size_t lds_allowed = 64 * 1024;
     if (lds > lds_allowed) {
         hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void *>(&stream_kernel<BC, R, P>),
+            reinterpret_cast<const void *>(&stream_kernel<BC, R, P, D2>),
             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
         lds_allowed = lds;
     }
     StreamArgs a{sh.x, sh.ldx, sh.W, sh.y, sh.ws, sh.N, sh.K, sh.B, ks, ksp, S};
-    hipLaunchKernelGGL((stream_kernel<BC, R, P>), dim3((unsigned)g, S), dim3(nw * 64), lds,
+    hipLaunchKernelGGL((stream_kernel<BC, R, P, D2>), dim3((unsigned)g, S), dim3(nw * 64), lds,
                        stream, a);
     return hipGetLastError();
 }
@@ -496,25 +758,72 @@ hipError_t launch_mfma_inst(const LaunchShape &sh, const proj_tactic_t &t,
     constexpr int P = mfma_ring(MT, NT);
     const int ks = slice_len(sh.K, t);
     const int S = slice_count(sh.K, t);
-    const int U = ceil_div_i(sh.N, 16 * NT);
-    int upw = 1;
-    if (t.wpc > 0) {
-        const long tw0 = std::max(1L, (long)sh.num_cus * t.wpc / S);
-        upw = ceil_div_i(U, tw0);
-    }
-    const int tw = ceil_div_i(U, upw);
     const int nw = std::min(t.waves, 4);
-    const int gx = ceil_div_i(tw, nw);
-    MfmaArgs a{sh.x, sh.ldx, sh.W, sh.y, sh.ws, sh.N, sh.K, sh.B, ks, upw, S};
-    hipLaunchKernelGGL((mfma_kernel<MT, NT, P>), dim3(gx, S), dim3(nw * 64), 0,
+    // workgroups: wpc waves per compute unit over the S slices (wpc 0 means
+    // one wave per 16*NT-row group), at most one per row
+    long g;
+    if (t.wpc > 0)
+        g = (long)sh.num_cus * t.wpc / (nw * (long)S);
+    else
+        g = ceil_div_i(ceil_div_i(sh.N, 16 * NT), nw);
+    g = std::max(1L, std::min(g, (long)sh.N));
+    const size_t lds = (size_t)nw * 2 * MT * NT * 256 * sizeof(float);
+    static size_t lds_allowed = 64 * 1024;
+    if (lds > lds_allowed) {
+        hipError_t e = hipFuncSetAttribute(
+            reinterpret_cast<const void *>(&mfma_kernel<MT, NT, P>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        lds_allowed = lds;
+    }
+    MfmaArgs a{sh.x, sh.ldx, sh.W, sh.y, sh.ws, sh.N, sh.K, sh.B, ks, S};
+    hipLaunchKernelGGL((mfma_kernel<MT, NT, P>), dim3((unsigned)g, S), dim3(nw * 64), lds,
                        stream, a);
     return hipGetLastError();
 }
 
+template <int MT, int NT>
+hipError_t launch_mfma_lds_inst(const LaunchShape &sh, const proj_tactic_t &t,
+                                hipStream_t stream) {
+    const int ks = slice_len(sh.K, t);
+    const int S = slice_count(sh.K, t);
+    const int nw = std::min(t.waves, 4);
+    long g;
+    if (t.wpc > 0)
+        g = (long)sh.num_cus * t.wpc / (nw * (long)S);
+    else
+        g = ceil_div_i(ceil_div_i(sh.N, 16 * NT), nw);
+    g = std::max(1L, std::min(g, (long)sh.N));
+    const size_t lds = mfma_lds_tile_bytes(t);
+    static size_t lds_allowed = 64 * 1024;
+    if (lds > lds_allowed) {
+        hipError_t e = hipFuncSetAttribute(
+            reinterpret_cast<const void *>(&mfma_lds_kernel<MT, NT>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        lds_allowed = lds;
+    }
+    MfmaArgs a{sh.x, sh.ldx, sh.W, sh.y, sh.ws, sh.N, sh.K, sh.B, ks, S};
+    hipLaunchKernelGGL((mfma_lds_kernel<MT, NT>), dim3((unsigned)g, S), dim3(nw * 64), lds,
+                       stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_mfma_lds(const LaunchShape &sh, const proj_tactic_t &t, hipStream_t st) {
+    if (t.bcap == 16 && t.rows == 1) return launch_mfma_lds_inst<1, 1>(sh, t, st);
+    if (t.bcap == 16 && t.rows == 2) return launch_mfma_lds_inst<1, 2>(sh, t, st);
+    if (t.bcap == 32 && t.rows == 1) return launch_mfma_lds_inst<2, 1>(sh, t, st);
+    if (t.bcap == 32 && t.rows == 2) return launch_mfma_lds_inst<2, 2>(sh, t, st);
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_stream(const LaunchShape &sh, const proj_tactic_t &t,
                          hipStream_t st) {
-#define TP1_STREAM_CASE(BC, R) \
-    if (t.bcap == BC && t.rows == R) return launch_stream_inst<BC, R>(sh, t, st);
+    const bool d2 = t.kernel == PROJ_KERNEL_STREAM_DOT2;
+#define TP1_STREAM_CASE(BC, R)                                                    \
+    if (t.bcap == BC && t.rows == R)                                              \
+        return d2 ? launch_stream_inst<BC, R, true>(sh, t, st)                    \
+                  : launch_stream_inst<BC, R, false>(sh, t, st);
     TP1_STREAM_CASE(1, 1) TP1_STREAM_CASE(1, 2) TP1_STREAM_CASE(1, 4)
     TP1_STREAM_CASE(2, 1) TP1_STREAM_CASE(2, 2) TP1_STREAM_CASE(2, 4)
     TP1_STREAM_CASE(4, 1) TP1_STREAM_CASE(4, 2) TP1_STREAM_CASE(4, 4)
@@ -540,10 +849,12 @@ hipError_t launch_mfma(const LaunchShape &sh, const proj_tactic_t &t, hipStream_
 hipError_t launch_projection(const LaunchShape &sh, const proj_tactic_t &t,
                              hipStream_t stream) {
     hipError_t e;
-    if (t.kernel == PROJ_KERNEL_STREAM)
+    if (t.kernel == PROJ_KERNEL_STREAM || t.kernel == PROJ_KERNEL_STREAM_DOT2)
         e = launch_stream(sh, t, stream);
     else if (t.kernel == PROJ_KERNEL_MFMA)
         e = launch_mfma(sh, t, stream);
+    else if (t.kernel == PROJ_KERNEL_MFMA_LDS)
+        e = launch_mfma_lds(sh, t, stream);
     else
         return hipErrorInvalidValue;
     if (e != hipSuccess) return e;
@@ -561,9 +872,14 @@ int kernel_name(int K, const proj_tactic_t &t, char *buf, size_t len) {
     if (!buf || len == 0) return -1;
     const bool split = slice_count(K, t) > 1;
     int n;
-    if (t.kernel == PROJ_KERNEL_STREAM)
-        n = snprintf(buf, len, "stream_kernel<%d, %d, %d>%s", t.bcap, t.rows,
-                     stream_ring(t.bcap, t.rows), split ? "+splitk_reduce" : "");
+    if (t.kernel == PROJ_KERNEL_STREAM || t.kernel == PROJ_KERNEL_STREAM_DOT2)
+        n = snprintf(buf, len, "stream_kernel<%d, %d, %d, %s>%s", t.bcap, t.rows,
+                     stream_ring(t.bcap, t.rows),
+                     t.kernel == PROJ_KERNEL_STREAM_DOT2 ? "true" : "false",
+                     split ? "+splitk_reduce" : "");
+    else if (t.kernel == PROJ_KERNEL_MFMA_LDS)
+        n = snprintf(buf, len, "mfma_lds_kernel<%d, %d>%s", t.bcap / 16, t.rows,
+                     split ? "+splitk_reduce" : "");
     else
         n = snprintf(buf, len, "mfma_kernel<%d, %d, %d>%s", t.bcap / 16, t.rows,
                      mfma_ring(t.bcap / 16, t.rows), split ? "+splitk_reduce" : "");

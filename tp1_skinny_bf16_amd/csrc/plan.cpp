@@ -46,7 +46,7 @@ int bin_index(const PlanCore &p, int B) {
 }
 
 bool tactic_instance_exists(const proj_tactic_t &t) {
-    if (t.kernel == PROJ_KERNEL_STREAM)
+    if (t.kernel == PROJ_KERNEL_STREAM || t.kernel == PROJ_KERNEL_STREAM_DOT2)
         return (t.bcap == 1 || t.bcap == 2 || t.bcap == 4 || t.bcap == 8) &&
                (t.rows == 1 || t.rows == 2 || t.rows == 4);
     if (t.kernel == PROJ_KERNEL_MFMA) {
@@ -56,12 +56,14 @@ bool tactic_instance_exists(const proj_tactic_t &t) {
         // 256 rows x 2+ N tiles would need 128+ accumulator registers.
         return m && n && !(t.bcap == 256 && t.rows > 1);
     }
+    if (t.kernel == PROJ_KERNEL_MFMA_LDS)
+        return (t.bcap == 16 || t.bcap == 32) && (t.rows == 1 || t.rows == 2);
     return false;
 }
 
 int slice_len(int K, const proj_tactic_t &t) {
     const int S = std::max(1, t.split);
-    const int step = t.kernel == PROJ_KERNEL_MFMA ? 32 : 8;
+    const int step = t.kernel == PROJ_KERNEL_MFMA ? 32 : 8;  // K per MFMA step
     int ks = ceil_div(K, S);
     ks = ceil_div(ks, step) * step;
     return std::max(ks, step);
@@ -77,6 +79,16 @@ size_t stream_lds_bytes(int K, const proj_tactic_t &t) {
     return (size_t)t.bcap * (size_t)ksp * 2u;
 }
 
+size_t mfma_lds_tile_bytes(const proj_tactic_t &t) {
+    // per wave: a 16*rows x 520 BF16 tile plus two partial tiles
+    return (size_t)t.waves * ((size_t)16 * t.rows * 520 * 2 +
+                              2u * (size_t)(t.bcap / 16) * (size_t)t.rows * 1024u);
+}
+
+size_t mfma_lds_bytes(const proj_tactic_t &t) {
+    return (size_t)t.waves * 2u * (size_t)(t.bcap / 16) * (size_t)t.rows * 1024u;
+}
+
 size_t tactic_workspace(int N, int K, const proj_tactic_t &t) {
     const int S = slice_count(K, t);
     if (S <= 1) return 0;
@@ -90,44 +102,53 @@ int check_tactic(int N, int K, int bin, const proj_tactic_t &t) {
     if (t.split < 1 || t.split > 64) return PROJ_EINVAL;
     if (t.waves < 1 || t.waves > kMaxWaves) return PROJ_EINVAL;
     if (t.wpc < 0 || t.wpc > 32) return PROJ_EINVAL;
-    if (t.kernel == PROJ_KERNEL_STREAM) {
+    if (t.kernel == PROJ_KERNEL_STREAM || t.kernel == PROJ_KERNEL_STREAM_DOT2) {
         if (t.wpc < 1 || t.waves > 8) return PROJ_EINVAL;
         if (stream_lds_bytes(K, t) > kLdsBytes) return PROJ_EINVAL;
     }
-    if (t.kernel == PROJ_KERNEL_MFMA && t.waves > 4) return PROJ_EINVAL;
+    if (t.kernel == PROJ_KERNEL_MFMA) {
+        if (t.waves > 4) return PROJ_EINVAL;
+        if (mfma_lds_bytes(t) > kLdsBytes) return PROJ_EINVAL;
+    }
+    if (t.kernel == PROJ_KERNEL_MFMA_LDS) {
+        if (t.waves > 4) return PROJ_EINVAL;
+        if (mfma_lds_tile_bytes(t) > kLdsBytes) return PROJ_EINVAL;
+    }
     return PROJ_OK;
 }
 
 proj_tactic_t default_tactic(int N, int K, int bin, int num_cus) {
+    // The rule the measured table follows on MI355X: the IEEE weight stream
+    // for 1-2 rows, MFMA from an LDS-transposed weight tile up to 32 rows,
+    // register-fed MFMA tiles above.
     proj_tactic_t t{};
     if (num_cus < 1) num_cus = 256;
-    if (bin <= 8) {
-        // Weight stream on the VALU: x staged in LDS per K slice.  Keep the
-        // slice small enough for two workgroups per compute unit.
+    (void)N;
+    if (bin <= 2) {
         t.kernel = PROJ_KERNEL_STREAM;
-        t.bcap = next_pow2(bin);
-        t.rows = t.bcap >= 4 ? 2 : 1;
+        t.bcap = bin;
+        t.rows = 4;
         t.waves = 4;
         t.wpc = 8;
-        const size_t budget = 80 * 1024;
-        int S = 1;
-        for (;; ++S) {
-            t.split = S;
-            if (stream_lds_bytes(K, t) <= budget || S >= 16) break;
-        }
-        (void)N;
+        t.split = 1;
+        while (stream_lds_bytes(K, t) > 80 * 1024 && t.split < 16) ++t.split;
         return t;
     }
-    // MFMA tiles: one wave per N range, split K until the chip is covered.
+    if (bin <= 32) {
+        t.kernel = PROJ_KERNEL_MFMA_LDS;
+        t.bcap = bin <= 16 ? 16 : 32;
+        t.rows = bin <= 8 ? 1 : 2;
+        t.waves = 1;
+        t.wpc = bin <= 8 ? 4 : 0;
+        t.split = 1;
+        return t;
+    }
     t.kernel = PROJ_KERNEL_MFMA;
-    t.bcap = std::max(16, next_pow2(bin));
-    t.rows = t.bcap >= 256 ? 1 : 2;
-    t.waves = 4;
-    t.wpc = 0;
-    const int units = ceil_div(N, 16 * t.rows);
-    int S = 1;
-    while ((long)units * S < 4L * num_cus && S < 8) ++S;
-    t.split = S;
+    t.bcap = next_pow2(bin);
+    t.rows = t.bcap >= 256 ? 1 : 4;
+    t.waves = t.bcap >= 256 ? 4 : 2;
+    t.wpc = t.bcap >= 256 ? 4 : 2;
+    t.split = t.bcap >= 256 ? 1 : 2;
     return t;
 }
 

@@ -49,6 +49,12 @@ int slice_len(int K, const proj_tactic_t &t);
 // Number of K slices actually launched (ceil(K / slice_len)).
 int slice_count(int K, const proj_tactic_t &t);
 
+// LDS bytes of an MFMA_LDS tactic's per-wave tiles and partial tiles.
+size_t mfma_lds_tile_bytes(const proj_tactic_t &t);
+
+// LDS bytes of an MFMA tactic's per-wave partial tiles.
+size_t mfma_lds_bytes(const proj_tactic_t &t);
+
 // LDS bytes a STREAM tactic stages x into.
 size_t stream_lds_bytes(int K, const proj_tactic_t &t);
 

@@ -106,7 +106,8 @@ int proj_plan(int N, int K, const int *batches, int n_batches, unsigned flags,
     // further until the staged x slice fits.
     for (int i = 0; i < p->core.nb; ++i) {
         proj_tactic_t &t = p->core.tactics[i];
-        while (t.kernel == PROJ_KERNEL_STREAM && t.split < 64 &&
+        while ((t.kernel == PROJ_KERNEL_STREAM || t.kernel == PROJ_KERNEL_STREAM_DOT2) &&
+               t.split < 64 &&
                tp1::stream_lds_bytes(K, t) > p->lds_limit)
             ++t.split;
     }
@@ -149,8 +150,13 @@ int proj_plan_set_tactic(proj_plan_t *plan, int bin, const proj_tactic_t *tactic
     if (i < 0) return PROJ_EINVAL;
     if (tp1::check_tactic(plan->core.N, plan->core.K, bin, *tactic) != PROJ_OK)
         return PROJ_EINVAL;
-    if (tactic->kernel == PROJ_KERNEL_STREAM &&
+    if ((tactic->kernel == PROJ_KERNEL_STREAM || tactic->kernel == PROJ_KERNEL_STREAM_DOT2) &&
         tp1::stream_lds_bytes(plan->core.K, *tactic) > plan->lds_limit)
+        return PROJ_EINVAL;
+    if (tactic->kernel == PROJ_KERNEL_MFMA && tp1::mfma_lds_bytes(*tactic) > plan->lds_limit)
+        return PROJ_EINVAL;
+    if (tactic->kernel == PROJ_KERNEL_MFMA_LDS &&
+        tp1::mfma_lds_tile_bytes(*tactic) > plan->lds_limit)
         return PROJ_EINVAL;
     const int rc = alloc_workspace(plan, tp1::tactic_workspace(plan->core.N, plan->core.K, *tactic));
     if (rc != PROJ_OK) return rc;

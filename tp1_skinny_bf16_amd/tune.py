@@ -21,7 +21,8 @@ import time
 
 import torch
 
-from . import KERNEL_MFMA, KERNEL_STREAM, Plan, ProjError, Tactic
+from . import (KERNEL_IDS, KERNEL_MFMA, KERNEL_MFMA_LDS, KERNEL_STREAM, KERNEL_STREAM_DOT2,
+               Plan, ProjError, Tactic)
 from .timing import gbs, rotation_copies, time_calls
 
 SHAPES = {"dsa": (14560, 7168), "oproj": (7168, 12288), "kda": (49376, 7168)}
@@ -38,18 +39,24 @@ def candidates(bin_: int, full: bool = False):
     out = []
     if bin_ <= 8:
         bc = next_pow2(bin_)
-        for rows, split, waves, wpc in itertools.product(
-                (1, 2, 4), (1, 2, 3, 4), (1, 2, 4, 8), (2, 4, 6, 8, 12, 16)):
-            if not full and waves == 8 and wpc < 8:
+        for kern, rows, split, waves, wpc in itertools.product(
+                (KERNEL_STREAM, KERNEL_STREAM_DOT2), (1, 2, 4), (1, 2, 3, 4),
+                (1, 2, 4, 8), (2, 4, 6, 8, 12, 16)):
+            if not full and (waves == 8 and wpc < 8 or split > 2):
                 continue
-            out.append(Tactic(KERNEL_STREAM, bc, split, rows, waves, wpc))
-    if bin_ >= 2:
+            out.append(Tactic(kern, bc, split, rows, waves, wpc))
+    if True:
         bc = max(16, next_pow2(bin_))
         for rows, split, waves, wpc in itertools.product(
                 (1, 2, 4), (1, 2, 3, 4, 6), (1, 2, 4), (0, 2, 4, 8)):
             if bc == 256 and rows > 1:
                 continue
             out.append(Tactic(KERNEL_MFMA, bc, split, rows, waves, wpc))
+    if bin_ <= 32:
+        bc = 16 if bin_ <= 16 else 32
+        for rows, split, waves, wpc in itertools.product(
+                (1, 2), (1, 2), (1, 2, 3, 4), (0, 2, 4, 6, 8, 12)):
+            out.append(Tactic(KERNEL_MFMA_LDS, bc, split, rows, waves, wpc))
     return out
 
 
@@ -93,9 +100,9 @@ def measure(N: int, K: int, bins, reps: int = 40, log=None, full: bool = False):
         nbytes = 2 * N * K + 2 * b * K + 2 * b * N
         result["bins"][b] = {"chosen": chosen, "GBps": round(gbs(nbytes, chosen["us"]), 1),
                              "top": rows[:8], "n_candidates": len(rows)}
-        best_stream = min((r for r in rows if r["tactic"]["kernel"] == "stream"),
+        best_stream = min((r for r in rows if r["tactic"]["kernel"].startswith("stream")),
                           key=lambda r: r["us"], default=None)
-        best_mfma = min((r for r in rows if r["tactic"]["kernel"] == "mfma"),
+        best_mfma = min((r for r in rows if r["tactic"]["kernel"].startswith("mfma")),
                         key=lambda r: r["us"], default=None)
         result["bins"][b]["best_stream_us"] = best_stream["us"] if best_stream else None
         result["bins"][b]["best_mfma_us"] = best_mfma["us"] if best_mfma else None
@@ -104,9 +111,9 @@ def measure(N: int, K: int, bins, reps: int = 40, log=None, full: bool = False):
                 f"{chosen['kernel']} {chosen['tactic']} (stream {result['bins'][b]['best_stream_us']}"
                 f" / mfma {result['bins'][b]['best_mfma_us']}, {len(rows)} candidates)")
         plan.set_tactic(b, Tactic(**{**chosen["tactic"],
-                                     "kernel": KERNEL_STREAM if chosen["tactic"]["kernel"] == "stream"
-                                     else KERNEL_MFMA}))
-    mfma_bins = [b for b in bins if result["bins"][b]["chosen"]["tactic"]["kernel"] == "mfma"]
+                                     "kernel": KERNEL_IDS[chosen["tactic"]["kernel"]]}))
+    mfma_bins = [b for b in bins
+                 if result["bins"][b]["chosen"]["tactic"]["kernel"].startswith("mfma")]
     result["crossover"] = min(mfma_bins) if mfma_bins else None
     return result
 
@@ -115,14 +122,70 @@ def table_rows(result) -> str:
     lines = []
     for b, r in result["bins"].items():
         t = r["chosen"]["tactic"]
-        k = "PROJ_KERNEL_STREAM" if t["kernel"] == "stream" else "PROJ_KERNEL_MFMA"
+        k = {"stream": "PROJ_KERNEL_STREAM", "mfma": "PROJ_KERNEL_MFMA",
+             "stream_dot2": "PROJ_KERNEL_STREAM_DOT2",
+             "mfma_lds": "PROJ_KERNEL_MFMA_LDS"}[t["kernel"]]
         lines.append(f"    {{{result['N']}, {result['K']}, {b}, {{{k}, {t['bcap']}, {t['split']}, "
                      f"{t['rows']}, {t['waves']}, {t['wpc']}}}}},  // {r['chosen']['us']} us, "
                      f"{r['GBps']} GB/s")
     return "\n".join(lines)
 
 
+def emit_table(paths) -> str:
+    """C++ rows of tactics_table.cpp from tuner JSON files (later files win)."""
+    chosen = {}
+    for path in paths:
+        with open(path) as f:
+            for res in json.load(f):
+                for b, r in res["bins"].items():
+                    chosen[(res["N"], res["K"], int(b))] = r
+    merged = {}
+    for (N, K, b), r in chosen.items():
+        merged.setdefault((N, K), {"N": N, "K": K, "bins": {}})["bins"][b] = r
+    out = []
+    for key in sorted(merged):
+        res = merged[key]
+        res["bins"] = dict(sorted(res["bins"].items()))
+        out.append(table_rows(res))
+    return "\n".join(out)
+
+
+def summarize(paths) -> str:
+    """Markdown of the measured tables: chosen tactic per bin, the best stream
+    and best MFMA candidate, and the crossover (later files win)."""
+    chosen = {}
+    for path in paths:
+        with open(path) as f:
+            for res in json.load(f):
+                for b, r in res["bins"].items():
+                    chosen[(res["N"], res["K"], int(b))] = r
+    lines = []
+    for (N, K) in sorted({(n, k) for n, k, _ in chosen}):
+        bins = sorted(b for n, k, b in chosen if (n, k) == (N, K))
+        lines += [f"## {N} x {K}", "",
+                  "| bin | chosen kernel | tactic (bcap, split, rows, waves, wpc) | us | GB/s "
+                  "| best stream us | best MFMA us | candidates |",
+                  "|---|---|---|---|---|---|---|---|"]
+        cross = None
+        for b in bins:
+            r = chosen[(N, K, b)]
+            t = r["chosen"]["tactic"]
+            if cross is None and t["kernel"].startswith("mfma"):
+                cross = b
+            lines.append(f"| {b} | `{r['chosen']['kernel']}` | {t['bcap']}, {t['split']}, {t['rows']}, "
+                         f"{t['waves']}, {t['wpc']} | {r['chosen']['us']} | {r['GBps']} | "
+                         f"{r.get('best_stream_us')} | {r.get('best_mfma_us')} | {r['n_candidates']} |")
+        lines += ["", f"Crossover (first bin whose best tactic is an MFMA kernel): {cross}", ""]
+    return "\n".join(lines)
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--emit-table":
+        print(emit_table(sys.argv[2:]))
+        return 0
+    if len(sys.argv) > 1 and sys.argv[1] == "--summarize":
+        print(summarize(sys.argv[2:]))
+        return 0
     ap = argparse.ArgumentParser()
     ap.add_argument("--shape", action="append", required=True,
                     help="NxK or one of " + ",".join(SHAPES))

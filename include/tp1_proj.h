@@ -52,9 +52,14 @@ enum proj_kernel {
     PROJ_KERNEL_STREAM_DOT2 = 3, /* the weight stream with v_dot2 BF16 pair
                                products: FP32 accumulation whose additions
                                are not always IEEE round-to-nearest      */
-    PROJ_KERNEL_MFMA_LDS = 4 /* MFMA tiles fed from a per-wave LDS tile that
+    PROJ_KERNEL_MFMA_LDS = 4, /* MFMA tiles fed from a per-wave LDS tile that
                                the weight reaches with 1 KB row loads
                                (bcap 16 or 32, rows 1 or 2)              */
+    PROJ_KERNEL_MFMA_XS = 5  /* large batches: x and W chunk tiles staged
+                               once per workgroup in LDS and shared by its
+                               4 waves (bcap 64/128/256; rows = N tiles
+                               per group, 2 or 4; waves = waves along the
+                               batch, 1/2/4; wpc = workgroups per CU)    */
 };
 
 /* Plan flags. */
@@ -62,6 +67,14 @@ enum proj_kernel {
                                     without touching a device: the plan can
                                     be queried but proj_run returns
                                     PROJ_ENODEV                             */
+#define PROJ_PLAN_SPLIT_FUSED 0x2u /* reduce split-K partials inside the
+                                    producing kernel (the last workgroup of a
+                                    row range to arrive sums the slices)
+                                    instead of with a second kernel; both add
+                                    the slices in the fixed order s = 0..S-1,
+                                    so results are equal bit for bit.  Slower
+                                    on MI355X as measured: each workgroup's
+                                    device-wide release writes its L2 back */
 
 /* Limits checked by proj_plan. */
 #define PROJ_MAX_BATCH 256       /* largest batch a plan may list          */
@@ -80,6 +93,7 @@ enum proj_kernel {
  *            tiles must fit the LDS: waves * 2 * bcap/16 * rows KB <= 160)
  *   wpc    : STREAM: waves per compute unit the grid is sized for
  *            MFMA:   0 = one wave per N range (grid from N), else as STREAM
+ *   kc     : MFMA_XS: K chunk staged per step (128 or 256); 0 elsewhere
  */
 typedef struct proj_tactic {
     int kernel;
@@ -88,6 +102,7 @@ typedef struct proj_tactic {
     int rows;
     int waves;
     int wpc;
+    int kc;
 } proj_tactic_t;
 
 typedef struct proj_plan_s proj_plan_t;
@@ -97,10 +112,12 @@ typedef struct proj_plan_s proj_plan_t;
  *   N, K      : weight rows / columns; N > 0, K > 0, K % 8 == 0
  *   batches   : strictly increasing, 1 <= b <= PROJ_MAX_BATCH, length
  *               1..PROJ_MAX_BATCHES (host array, not retained)
- *   flags     : 0 or PROJ_PLAN_HOST_ONLY
+ *   flags     : 0 or a combination of PROJ_PLAN_HOST_ONLY and
+ *               PROJ_PLAN_SPLIT_FUSED
  *   out       : receives the plan (set to NULL on failure)
- * The plan owns an FP32 split-K workspace allocated with hipMalloc on the
- * current device (none for host-only plans); proj_free releases it.
+ * The plan owns an FP32 split-K workspace and (with PROJ_PLAN_SPLIT_FUSED)
+ * 256 KiB of zeroed arrival counters, allocated with hipMalloc on the
+ * current device (none for host-only plans); proj_free releases them.
  * Returns PROJ_OK, PROJ_EINVAL, PROJ_ENOMEM or PROJ_EHIP.
  */
 int proj_plan(int N, int K, const int *batches, int n_batches, unsigned flags,

@@ -228,3 +228,33 @@ def test_multilayer_stream_per_layer_parity():
         check_random(f"layer {l} o_proj", wl.bits(y_o[l]), xo, t["W_o"][l], cols=cols)
         x_l = y_o[l]
     say(f"final |y| rms = {float(y_o[-1].float().pow(2).mean().sqrt()):.4g}")
+
+
+def test_fused_split_matches_two_pass_bitwise():
+    """The in-kernel split-K reduction (last workgroup to arrive sums the
+    slices) and the two-pass reduction add the slices in the same order, so
+    they agree bit for bit; repeated calls also check that the arrival
+    counters are left at zero."""
+    N, K = 2000, 3072
+    x, W = wl.random_case(64, N, K, seed=21)
+    Wd = W.to(DEV)
+    fused = tp.Plan(N, K, [4, 16, 64], fused_split=True)
+    twop = tp.Plan(N, K, [4, 16, 64])
+    tactics = [(4, tp.Tactic(tp.KERNEL_STREAM, 4, 3, 2, 4, 8)),
+               (4, tp.Tactic(tp.KERNEL_STREAM_DOT2, 4, 2, 4, 2, 4)),
+               (16, tp.Tactic(tp.KERNEL_MFMA_LDS, 16, 2, 1, 2, 4)),
+               (16, tp.Tactic(tp.KERNEL_MFMA, 16, 3, 2, 4, 0)),
+               (16, tp.Tactic(tp.KERNEL_MFMA_XS, 16, 4, 8, 1, 2, 128)),
+               (64, tp.Tactic(tp.KERNEL_MFMA_XS, 64, 3, 4, 4, 2, 128))]
+    for bin_, t in tactics:
+        fused.set_tactic(bin_, t)
+        twop.set_tactic(bin_, t)
+        assert "+splitk_reduce" not in fused.kernel_name(bin_)
+        assert twop.kernel_name(bin_).endswith("+splitk_reduce")
+        for B in (bin_, max(1, bin_ - 3)):
+            a1 = gpu_run(fused, x[:B], Wd)
+            a2 = gpu_run(fused, x[:B], Wd)
+            b1 = gpu_run(twop, x[:B], Wd)
+            assert np.array_equal(a1, a2), f"{t} B={B}: fused not reproducible"
+            assert np.array_equal(a1, b1), f"{t} B={B}: fused != two-pass"
+            check_random(f"fused split {tactic_label(fused, B)} B={B}", a1, x[:B], W)

@@ -26,11 +26,13 @@ KERNEL_STREAM = 1
 KERNEL_MFMA = 2
 KERNEL_STREAM_DOT2 = 3
 KERNEL_MFMA_LDS = 4
+KERNEL_MFMA_XS = 5
 KERNEL_NAMES = {KERNEL_STREAM: "stream", KERNEL_MFMA: "mfma", KERNEL_STREAM_DOT2: "stream_dot2",
-                KERNEL_MFMA_LDS: "mfma_lds"}
+                KERNEL_MFMA_LDS: "mfma_lds", KERNEL_MFMA_XS: "mfma_xs"}
 KERNEL_IDS = {v: k for k, v in KERNEL_NAMES.items()}
 
 PLAN_HOST_ONLY = 0x1
+PLAN_SPLIT_FUSED = 0x2
 MAX_BATCH = 256
 MAX_BATCHES = 64
 
@@ -51,7 +53,7 @@ class ProjError(RuntimeError):
 class _Tactic(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int), ("bcap", ctypes.c_int),
                 ("split", ctypes.c_int), ("rows", ctypes.c_int),
-                ("waves", ctypes.c_int), ("wpc", ctypes.c_int)]
+                ("waves", ctypes.c_int), ("wpc", ctypes.c_int), ("kc", ctypes.c_int)]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -62,6 +64,7 @@ class Tactic:
     rows: int
     waves: int
     wpc: int
+    kc: int = 0
 
     @property
     def kernel_name(self) -> str:
@@ -74,7 +77,7 @@ class Tactic:
 
     def _c(self) -> _Tactic:
         return _Tactic(self.kernel, self.bcap, self.split, self.rows, self.waves,
-                       self.wpc)
+                       self.wpc, self.kc)
 
 
 _LIB = None
@@ -147,13 +150,14 @@ class Plan:
     y = x . W^T into `out` (BF16 [B, N]) and returns it.
     """
 
-    def __init__(self, N: int, K: int, batches, *, host_only: bool = False):
+    def __init__(self, N: int, K: int, batches, *, host_only: bool = False,
+                 fused_split: bool = False):
         self.N, self.K = int(N), int(K)
         self.batches = tuple(int(b) for b in batches)
         arr = (ctypes.c_int * max(1, len(self.batches)))(*self.batches)
         h = ctypes.c_void_p()
-        rc = _lib().proj_plan(self.N, self.K, arr, len(self.batches),
-                              PLAN_HOST_ONLY if host_only else 0, ctypes.byref(h))
+        flags = (PLAN_HOST_ONLY if host_only else 0) | (PLAN_SPLIT_FUSED if fused_split else 0)
+        rc = _lib().proj_plan(self.N, self.K, arr, len(self.batches), flags, ctypes.byref(h))
         _check(rc, f"proj_plan(N={N}, K={K}, batches={self.batches})")
         self._h = h
         self.host_only = host_only
@@ -189,7 +193,7 @@ class Plan:
         b = ctypes.c_int()
         _check(_lib().proj_plan_tactic(self._h, int(B), ctypes.byref(t), ctypes.byref(b)),
                f"proj_plan_tactic(B={B})")
-        return Tactic(t.kernel, t.bcap, t.split, t.rows, t.waves, t.wpc), b.value
+        return Tactic(t.kernel, t.bcap, t.split, t.rows, t.waves, t.wpc, t.kc), b.value
 
     def kernel_name(self, B: int) -> str:
         """Kernel instance(s) proj_run launches for batch B (profiler names)."""

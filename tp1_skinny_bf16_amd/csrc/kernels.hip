@@ -92,6 +92,41 @@ __device__ __forceinline__ float wave_sum(float v) {
 }
 
 // ---------------------------------------------------------------------------
+// Fused split-K reduction.  When K is split over S workgroups (gridDim.y),
+// each workgroup writes its FP32 partials for rows [row0, row0 + rows) to
+// the workspace, makes them visible device-wide, and counts its arrival on
+// an integer counter of its row range.  The workgroup that arrives last sums
+// the S partials in the fixed order s = 0..S-1 (the same order as the
+// two-pass splitk_reduce, so the result does not depend on arrival order),
+// rounds once to BF16, and resets the counter for the next call.  Called by
+// every thread of the workgroup, after its last partial store.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void splitk_fixup(const float *ws, uint16_t *y, int *cnt, int N,
+                                             int B, int row0, int rows) {
+    __shared__ int last;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // partials before the arrival
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        const int old = __hip_atomic_fetch_add(cnt + blockIdx.x, 1, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT);
+        last = old == (int)gridDim.y - 1;
+    }
+    __syncthreads();
+    if (!last) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // the other slices' partials
+    const int S = gridDim.y;
+    const size_t slice = (size_t)B * N;
+    for (int i = threadIdx.x; i < rows * B; i += blockDim.x) {
+        const int b = i / rows, r = i - (i / rows) * rows;
+        const size_t o = (size_t)b * N + row0 + r;
+        float acc = ws[o];
+        for (int k = 1; k < S; ++k) acc += ws[k * slice + o];
+        y[o] = to_bf16(acc);
+    }
+    if (threadIdx.x == 0) cnt[blockIdx.x] = 0;
+}
+
+// ---------------------------------------------------------------------------
 // Weight-stream kernel (small batches).
 //
 // Workgroup g owns rows [N*g/G, N*(g+1)/G) of W (so workgroups differ by at
@@ -116,6 +151,7 @@ struct StreamArgs {
     const uint16_t *W;
     uint16_t *y;
     float *ws;
+    int *cnt;   // split-K arrival counters (fused reduction) or nullptr
     int N, K, B;
     int ks;   // K elements per slice (multiple of 8)
     int ksp;  // LDS row pitch of the staged x slice (multiple of 512)
@@ -302,6 +338,7 @@ __global__ __launch_bounds__(512) void stream_kernel(StreamArgs a) {
             if (row < rows && b < a.B) store_out(row0 + row, b, sum);
         }
     }
+    if (a.S > 1 && a.cnt) splitk_fixup(a.ws, a.y, a.cnt, a.N, a.B, row0, rows);
 }
 
 // ---------------------------------------------------------------------------
@@ -330,6 +367,7 @@ struct MfmaArgs {
     const uint16_t *W;
     uint16_t *y;
     float *ws;
+    int *cnt;   // split-K arrival counters (fused reduction) or nullptr
     int N, K, B;
     int ks;    // K elements per slice (multiple of 32)
     int S;
@@ -484,6 +522,7 @@ __global__ __launch_bounds__(256) void mfma_kernel(MfmaArgs a) {
             if (b < a.B && r < rows) store_out(b, row0 + r, sum);
         }
     }
+    if (a.S > 1 && a.cnt) splitk_fixup(a.ws, a.y, a.cnt, a.N, a.B, row0, rows);
 }
 
 // ---------------------------------------------------------------------------
@@ -664,6 +703,142 @@ __global__ __launch_bounds__(256) void mfma_lds_kernel(MfmaArgs a) {
             if (b < a.B && r < rows) store_out(b, row0 + r, sum);
         }
     }
+    if (a.S > 1 && a.cnt) splitk_fixup(a.ws, a.y, a.cnt, a.N, a.B, row0, rows);
+}
+
+// ---------------------------------------------------------------------------
+// Shared-tile MFMA kernel (large batches).
+// A workgroup of 4 waves owns rows [N*g/G, N*(g+1)/G) for one K slice and
+// walks them in groups of 16*NTB rows.  For each K chunk (128 or 256 wide)
+// the workgroup stages the x tile (all 16*MT batch rows) and the W tile (the
+// group's rows) in LDS once, both with 256- or 512-byte row pieces,
+// and every wave reads its A and B fragments from there: the waves split
+// the tile WM x (4/WM), so each holds (MT/WM) x (NTB*WM/4) accumulator tiles
+// and reuses each fragment across them.  The next chunk is loaded into
+// registers while this one is multiplied; two barriers per chunk.  LDS rows
+// are padded by 16 bytes so the 16 rows of a fragment read fall in distinct
+// banks.
+// ---------------------------------------------------------------------------
+template <int MT, int NTB, int WM, int kXsChunk>
+__global__ __launch_bounds__(256) void mfma_xs_kernel(MfmaArgs a) {
+    constexpr int kXsPitch = kXsChunk + 8;   // bf16 per LDS row (16 bytes of pad)
+    constexpr int WN = 4 / WM;
+    constexpr int MTW = MT / WM;             // A tiles per wave
+    constexpr int NTW = NTB / WN;            // B tiles per wave
+    constexpr int GR = 16 * NTB;             // rows per group
+    constexpr int XV = MT * 16 * kXsChunk / 8 / 256;  // x vectors per thread per chunk
+    constexpr int WV = GR * kXsChunk / 8 / 256;       // W vectors per thread per chunk
+    static_assert((MT * 16 * kXsChunk / 8) % 256 == 0 && (GR * kXsChunk / 8) % 256 == 0,
+                  "tiles must split evenly over the workgroup");
+    static_assert(MT % WM == 0 && NTB % WN == 0, "tile split");
+    static_assert(XV >= 1 && WV >= 1, "chunk too small for the workgroup");
+    extern __shared__ __align__(16) uint16_t xs_lds[];
+    uint16_t *xt = xs_lds;                               // [16*MT][kXsPitch]
+    uint16_t *wt = xs_lds + MT * 16 * kXsPitch;          // [GR][kXsPitch]
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = uniform(tid >> 6);
+    const int wm = wave / WN, wn = wave - (wave / WN) * WN;
+    const int s = blockIdx.y;
+    const int k0 = s * a.ks;
+    const int klen = min(a.K - k0, a.ks);
+    const int row0 = (int)((long)a.N * blockIdx.x / gridDim.x);
+    const int rows = (int)((long)a.N * (blockIdx.x + 1) / gridDim.x) - row0;
+    const int C = (klen + kXsChunk - 1) / kXsChunk;
+    const int Gb = (rows + GR - 1) / GR;
+    const int lrow = lane & 15, lgrp = lane >> 4;
+    // cooperative load mapping: kXsChunk/8 lanes cover one row piece
+    constexpr int LPR = kXsChunk / 8;           // lanes per row piece
+    constexpr int RPS = 256 / LPR;              // rows per pass of the workgroup
+    const int prow = tid / LPR;                 // row within a pass
+    const int pk = (tid % LPR) * 8;             // K offset within the chunk
+
+    auto store_out = [&](int row, int col, float v) {
+        if (a.S == 1)
+            a.y[(size_t)row * a.N + col] = to_bf16(v);
+        else
+            a.ws[((size_t)s * a.B + row) * a.N + col] = v;
+    };
+
+    u32x4 xr[XV], wr[WV];
+    auto load_chunk = [&](int g, int c) {
+        const int kk = min(c * kXsChunk + pk, klen - 8);
+#pragma unroll
+        for (int i = 0; i < XV; ++i) {
+            const int b = min(i * RPS + prow, a.B - 1);
+            xr[i] = load_cached(a.x + (size_t)b * a.ldx + k0 + kk);
+        }
+#pragma unroll
+        for (int i = 0; i < WV; ++i) {
+            const int r = min(g * GR + i * RPS + prow, rows - 1);
+            wr[i] = load_stream(a.W + (size_t)(row0 + r) * a.K + k0 + kk);
+        }
+    };
+    auto store_chunk = [&](int c) {
+        const bool dead = c * kXsChunk + pk >= klen;   // past the slice
+#pragma unroll
+        for (int i = 0; i < XV; ++i)
+            *reinterpret_cast<u32x4 *>(xt + (i * RPS + prow) * kXsPitch + pk) = xr[i];
+#pragma unroll
+        for (int i = 0; i < WV; ++i)
+            *reinterpret_cast<u32x4 *>(wt + (i * RPS + prow) * kXsPitch + pk) =
+                dead ? u32x4{0u, 0u, 0u, 0u} : wr[i];
+    };
+
+    const int T = Gb * C;
+    if (T == 0) return;  // uniform over the workgroup: no barrier is skipped by part of it
+    f32x4 acc[MTW][NTW];
+#pragma unroll
+    for (int m = 0; m < MTW; ++m)
+#pragma unroll
+        for (int n = 0; n < NTW; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    load_chunk(0, 0);
+    int g = 0, c = 0;
+    for (int t = 0; t < T; ++t) {
+        __syncthreads();                 // every wave is done with the previous tiles
+        store_chunk(c);
+        __syncthreads();                 // tiles of step t visible
+        const int ng = (c + 1 == C) ? g + 1 : g;
+        const int nc = (c + 1 == C) ? 0 : c + 1;
+        if (t + 1 < T) load_chunk(ng, nc);   // uniform: next chunk into registers
+#pragma unroll
+        for (int j = 0; j < kXsChunk / 32; ++j) {
+            u32x4 bf[NTW];
+#pragma unroll
+            for (int n = 0; n < NTW; ++n)
+                bf[n] = *reinterpret_cast<const u32x4 *>(
+                    wt + ((wn * NTW + n) * 16 + lrow) * kXsPitch + j * 32 + lgrp * 8);
+#pragma unroll
+            for (int m = 0; m < MTW; ++m) {
+                const u32x4 af = *reinterpret_cast<const u32x4 *>(
+                    xt + ((wm * MTW + m) * 16 + lrow) * kXsPitch + j * 32 + lgrp * 8);
+#pragma unroll
+                for (int n = 0; n < NTW; ++n)
+                    acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8_t, af), __builtin_bit_cast(bf16x8_t, bf[n]),
+                        acc[m][n], 0, 0, 0);
+            }
+        }
+        if (c == C - 1) {
+#pragma unroll
+            for (int m = 0; m < MTW; ++m)
+#pragma unroll
+                for (int n = 0; n < NTW; ++n) {
+                    const int r = g * GR + (wn * NTW + n) * 16 + lrow;
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const int b = (wm * MTW + m) * 16 + lgrp * 4 + v;
+                        if (b < a.B && r < rows) store_out(b, row0 + r, acc[m][n][v]);
+                    }
+                    acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+        }
+        g = ng;
+        c = nc;
+    }
+    if (a.S > 1 && a.cnt) splitk_fixup(a.ws, a.y, a.cnt, a.N, a.B, row0, rows);
 }
 
 // ---------------------------------------------------------------------------
@@ -709,6 +884,35 @@ namespace {
 
 int ceil_div_i(long a, long b) { return (int)((a + b - 1) / b); }
 
+// Counters for the fused split-K reduction of a launch with gx workgroups
+// per slice, or nullptr when the launch is not split or the plan reduces in
+// a second pass (the caller then launches splitk_reduce).
+int *fused_counters(const LaunchShape &sh, long gx, int S) {
+    return (S > 1 && sh.cnt && gx <= kSplitCounters) ? sh.cnt : nullptr;
+}
+
+// Workgroups per K slice of a launch (gridDim.x): wpc waves (STREAM, MFMA,
+// MFMA_LDS) or workgroups (MFMA_XS) per compute unit over the S slices; for
+// MFMA / MFMA_LDS, wpc 0 means one wave per 16*rows-row group.  At most one
+// workgroup per row.
+long grid_x(const LaunchShape &sh, const proj_tactic_t &t) {
+    const int S = slice_count(sh.K, t);
+    long g;
+    if (t.kernel == PROJ_KERNEL_STREAM || t.kernel == PROJ_KERNEL_STREAM_DOT2) {
+        const int nw = std::min(t.waves, kStreamMaxWaves);
+        g = (long)sh.num_cus * t.wpc / (nw * (long)S);
+    } else if (t.kernel == PROJ_KERNEL_MFMA_XS) {
+        g = (long)sh.num_cus * std::max(1, t.wpc) / S;
+    } else {
+        const int nw = std::min(t.waves, 4);
+        if (t.wpc > 0)
+            g = (long)sh.num_cus * t.wpc / (nw * (long)S);
+        else
+            g = ceil_div_i(ceil_div_i(sh.N, 16 * t.rows), nw);
+    }
+    return std::max(1L, std::min(g, (long)sh.N));
+}
+
 // Weight loads in flight per lane: 16 for narrow batches, fewer when the
 // accumulators of a wide batch need the registers.
 constexpr int stream_ring(int BC, int R) {
@@ -730,10 +934,7 @@ hipError_t launch_stream_inst(const LaunchShape &sh, const proj_tactic_t &t,
     const int S = slice_count(sh.K, t);
     const int ksp = ceil_div_i(ks, kStreamChunk) * kStreamChunk;
     const int nw = std::min(t.waves, kStreamMaxWaves);
-    // workgroups: wpc waves per compute unit over the S slices, at most one
-    // per row
-    long g = (long)sh.num_cus * t.wpc / (nw * (long)S);
-    g = std::max(1L, std::min(g, (long)sh.N));
+    const long g = grid_x(sh, t);
     const size_t lds = (size_t)BC * ksp * 2;
 
     // Dynamic LDS above 64 KB has to be allowed per kernel; raise the limit
@@ -746,7 +947,8 @@ hipError_t launch_stream_inst(const LaunchShape &sh, const proj_tactic_t &t,
         if (e != hipSuccess) return e;
         lds_allowed = lds;
     }
-    StreamArgs a{sh.x, sh.ldx, sh.W, sh.y, sh.ws, sh.N, sh.K, sh.B, ks, ksp, S};
+    StreamArgs a{sh.x, sh.ldx, sh.W, sh.y, sh.ws, fused_counters(sh, g, S), sh.N, sh.K, sh.B,
+                 ks, ksp, S};
     hipLaunchKernelGGL((stream_kernel<BC, R, P, D2>), dim3((unsigned)g, S), dim3(nw * 64), lds,
                        stream, a);
     return hipGetLastError();
@@ -759,14 +961,7 @@ hipError_t launch_mfma_inst(const LaunchShape &sh, const proj_tactic_t &t,
     const int ks = slice_len(sh.K, t);
     const int S = slice_count(sh.K, t);
     const int nw = std::min(t.waves, 4);
-    // workgroups: wpc waves per compute unit over the S slices (wpc 0 means
-    // one wave per 16*NT-row group), at most one per row
-    long g;
-    if (t.wpc > 0)
-        g = (long)sh.num_cus * t.wpc / (nw * (long)S);
-    else
-        g = ceil_div_i(ceil_div_i(sh.N, 16 * NT), nw);
-    g = std::max(1L, std::min(g, (long)sh.N));
+    const long g = grid_x(sh, t);
     const size_t lds = (size_t)nw * 2 * MT * NT * 256 * sizeof(float);
     static size_t lds_allowed = 64 * 1024;
     if (lds > lds_allowed) {
@@ -776,7 +971,8 @@ hipError_t launch_mfma_inst(const LaunchShape &sh, const proj_tactic_t &t,
         if (e != hipSuccess) return e;
         lds_allowed = lds;
     }
-    MfmaArgs a{sh.x, sh.ldx, sh.W, sh.y, sh.ws, sh.N, sh.K, sh.B, ks, S};
+    MfmaArgs a{sh.x, sh.ldx, sh.W, sh.y, sh.ws, fused_counters(sh, g, S), sh.N, sh.K, sh.B,
+               ks, S};
     hipLaunchKernelGGL((mfma_kernel<MT, NT, P>), dim3((unsigned)g, S), dim3(nw * 64), lds,
                        stream, a);
     return hipGetLastError();
@@ -788,12 +984,7 @@ hipError_t launch_mfma_lds_inst(const LaunchShape &sh, const proj_tactic_t &t,
     const int ks = slice_len(sh.K, t);
     const int S = slice_count(sh.K, t);
     const int nw = std::min(t.waves, 4);
-    long g;
-    if (t.wpc > 0)
-        g = (long)sh.num_cus * t.wpc / (nw * (long)S);
-    else
-        g = ceil_div_i(ceil_div_i(sh.N, 16 * NT), nw);
-    g = std::max(1L, std::min(g, (long)sh.N));
+    const long g = grid_x(sh, t);
     const size_t lds = mfma_lds_tile_bytes(t);
     static size_t lds_allowed = 64 * 1024;
     if (lds > lds_allowed) {
@@ -803,7 +994,8 @@ hipError_t launch_mfma_lds_inst(const LaunchShape &sh, const proj_tactic_t &t,
         if (e != hipSuccess) return e;
         lds_allowed = lds;
     }
-    MfmaArgs a{sh.x, sh.ldx, sh.W, sh.y, sh.ws, sh.N, sh.K, sh.B, ks, S};
+    MfmaArgs a{sh.x, sh.ldx, sh.W, sh.y, sh.ws, fused_counters(sh, g, S), sh.N, sh.K, sh.B,
+               ks, S};
     hipLaunchKernelGGL((mfma_lds_kernel<MT, NT>), dim3((unsigned)g, S), dim3(nw * 64), lds,
                        stream, a);
     return hipGetLastError();
@@ -814,6 +1006,38 @@ hipError_t launch_mfma_lds(const LaunchShape &sh, const proj_tactic_t &t, hipStr
     if (t.bcap == 16 && t.rows == 2) return launch_mfma_lds_inst<1, 2>(sh, t, st);
     if (t.bcap == 32 && t.rows == 1) return launch_mfma_lds_inst<2, 1>(sh, t, st);
     if (t.bcap == 32 && t.rows == 2) return launch_mfma_lds_inst<2, 2>(sh, t, st);
+    return hipErrorInvalidValue;
+}
+
+template <int MT, int NTB, int WM, int KC>
+hipError_t launch_mfma_xs_inst(const LaunchShape &sh, const proj_tactic_t &t,
+                               hipStream_t stream) {
+    const int ks = slice_len(sh.K, t);
+    const int S = slice_count(sh.K, t);
+    const long g = grid_x(sh, t);
+    const size_t lds = mfma_xs_lds_bytes(t);
+    static size_t lds_allowed = 64 * 1024;
+    if (lds > lds_allowed) {
+        hipError_t e = hipFuncSetAttribute(
+            reinterpret_cast<const void *>(&mfma_xs_kernel<MT, NTB, WM, KC>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        lds_allowed = lds;
+    }
+    MfmaArgs a{sh.x, sh.ldx, sh.W, sh.y, sh.ws, fused_counters(sh, g, S), sh.N, sh.K, sh.B,
+               ks, S};
+    hipLaunchKernelGGL((mfma_xs_kernel<MT, NTB, WM, KC>), dim3((unsigned)g, S), dim3(256), lds,
+                       stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_mfma_xs(const LaunchShape &sh, const proj_tactic_t &t, hipStream_t st) {
+    // rows = N tiles per group (NTB); waves = waves along M (WM); kc = K chunk
+#define TP1_XS_CASE(BC, NTB, WM, KC) \
+    if (t.bcap == BC && t.rows == NTB && t.waves == WM && t.kc == KC) \
+        return launch_mfma_xs_inst<BC / 16, NTB, WM, KC>(sh, t, st);
+    TP1_XS_INSTANCES(TP1_XS_CASE)
+#undef TP1_XS_CASE
     return hipErrorInvalidValue;
 }
 
@@ -855,11 +1079,13 @@ hipError_t launch_projection(const LaunchShape &sh, const proj_tactic_t &t,
         e = launch_mfma(sh, t, stream);
     else if (t.kernel == PROJ_KERNEL_MFMA_LDS)
         e = launch_mfma_lds(sh, t, stream);
+    else if (t.kernel == PROJ_KERNEL_MFMA_XS)
+        e = launch_mfma_xs(sh, t, stream);
     else
         return hipErrorInvalidValue;
     if (e != hipSuccess) return e;
     const int S = slice_count(sh.K, t);
-    if (S > 1) {
+    if (S > 1 && !fused_counters(sh, grid_x(sh, t), S)) {
         const long count = (long)sh.B * sh.N;
         hipLaunchKernelGGL(splitk_reduce, dim3(ceil_div_i(count, 256)), dim3(256), 0,
                            stream, sh.ws, sh.y, count, S);
@@ -868,9 +1094,10 @@ hipError_t launch_projection(const LaunchShape &sh, const proj_tactic_t &t,
     return e;
 }
 
-int kernel_name(int K, const proj_tactic_t &t, char *buf, size_t len) {
+int kernel_name(const LaunchShape &sh, const proj_tactic_t &t, char *buf, size_t len) {
     if (!buf || len == 0) return -1;
-    const bool split = slice_count(K, t) > 1;
+    const int S = slice_count(sh.K, t);
+    const bool split = S > 1 && !fused_counters(sh, grid_x(sh, t), S);
     int n;
     if (t.kernel == PROJ_KERNEL_STREAM || t.kernel == PROJ_KERNEL_STREAM_DOT2)
         n = snprintf(buf, len, "stream_kernel<%d, %d, %d, %s>%s", t.bcap, t.rows,
@@ -880,6 +1107,9 @@ int kernel_name(int K, const proj_tactic_t &t, char *buf, size_t len) {
     else if (t.kernel == PROJ_KERNEL_MFMA_LDS)
         n = snprintf(buf, len, "mfma_lds_kernel<%d, %d>%s", t.bcap / 16, t.rows,
                      split ? "+splitk_reduce" : "");
+    else if (t.kernel == PROJ_KERNEL_MFMA_XS)
+        n = snprintf(buf, len, "mfma_xs_kernel<%d, %d, %d, %d>%s", t.bcap / 16, t.rows, t.waves,
+                     t.kc, split ? "+splitk_reduce" : "");
     else
         n = snprintf(buf, len, "mfma_kernel<%d, %d, %d>%s", t.bcap / 16, t.rows,
                      mfma_ring(t.bcap / 16, t.rows), split ? "+splitk_reduce" : "");

@@ -17,15 +17,21 @@ struct LaunchShape {
     const uint16_t *W;
     uint16_t *y;
     float *ws;          // split-K workspace (S * B * N floats) or nullptr
+    int *cnt;           // kSplitCounters zeroed ints for the fused split-K
+                        // reduction, or nullptr for the two-pass reduction
     int num_cus;
 };
+
+// Arrival counters a plan holds for the fused split-K reduction (one per
+// workgroup of a K slice); larger grids fall back to the two-pass reduction.
+constexpr long kSplitCounters = 65536;
 
 // Enqueue one projection with tactic t.  Returns a hipError_t.
 hipError_t launch_projection(const LaunchShape &s, const proj_tactic_t &t,
                              hipStream_t stream);
 
 // Name of the kernel instance(s) a tactic launches (for profiles).
-int kernel_name(int K, const proj_tactic_t &t, char *buf, size_t len);
+int kernel_name(const LaunchShape &sh, const proj_tactic_t &t, char *buf, size_t len);
 
 // Streaming-read probe (measurement aid).
 hipError_t launch_read_probe(const void *buf, size_t bytes, float *sink,

@@ -28,7 +28,7 @@ int check_plan_args(int N, int K, const int *batches, int n_batches,
     if (N <= 0 || K <= 0 || (K % 8) != 0) return PROJ_EINVAL;
     if (!batches || n_batches < 1 || n_batches > PROJ_MAX_BATCHES)
         return PROJ_EINVAL;
-    if (flags & ~PROJ_PLAN_HOST_ONLY) return PROJ_EINVAL;
+    if (flags & ~(PROJ_PLAN_HOST_ONLY | PROJ_PLAN_SPLIT_FUSED)) return PROJ_EINVAL;
     for (int i = 0; i < n_batches; ++i) {
         if (batches[i] < 1 || batches[i] > PROJ_MAX_BATCH) return PROJ_EINVAL;
         if (i > 0 && batches[i] <= batches[i - 1]) return PROJ_EINVAL;
@@ -58,12 +58,21 @@ bool tactic_instance_exists(const proj_tactic_t &t) {
     }
     if (t.kernel == PROJ_KERNEL_MFMA_LDS)
         return (t.bcap == 16 || t.bcap == 32) && (t.rows == 1 || t.rows == 2);
+    if (t.kernel == PROJ_KERNEL_MFMA_XS) {
+#define TP1_XS_MATCH(BC, NTB, WM, KC) \
+        if (t.bcap == BC && t.rows == NTB && t.waves == WM && t.kc == KC) return true;
+        TP1_XS_INSTANCES(TP1_XS_MATCH)
+#undef TP1_XS_MATCH
+        return false;
+    }
     return false;
 }
 
 int slice_len(int K, const proj_tactic_t &t) {
     const int S = std::max(1, t.split);
-    const int step = t.kernel == PROJ_KERNEL_MFMA ? 32 : 8;  // K per MFMA step
+    // K granularity of a slice: one MFMA step, one shared chunk, or 8
+    const int step = t.kernel == PROJ_KERNEL_MFMA ? 32
+                     : (t.kernel == PROJ_KERNEL_MFMA_XS ? std::max(t.kc, 32) : 8);
     int ks = ceil_div(K, S);
     ks = ceil_div(ks, step) * step;
     return std::max(ks, step);
@@ -77,6 +86,10 @@ size_t stream_lds_bytes(int K, const proj_tactic_t &t) {
     const int ks = slice_len(K, t);
     const int ksp = ceil_div(ks, kStreamChunk) * kStreamChunk;
     return (size_t)t.bcap * (size_t)ksp * 2u;
+}
+
+size_t mfma_xs_lds_bytes(const proj_tactic_t &t) {
+    return (size_t)(t.bcap + 16 * t.rows) * (size_t)(t.kc + 8) * 2u;
 }
 
 size_t mfma_lds_tile_bytes(const proj_tactic_t &t) {
@@ -114,16 +127,22 @@ int check_tactic(int N, int K, int bin, const proj_tactic_t &t) {
         if (t.waves > 4) return PROJ_EINVAL;
         if (mfma_lds_tile_bytes(t) > kLdsBytes) return PROJ_EINVAL;
     }
+    if (t.kernel == PROJ_KERNEL_MFMA_XS) {
+        if (t.wpc < 1 || t.wpc > 2) return PROJ_EINVAL;
+        if (mfma_xs_lds_bytes(t) > kLdsBytes) return PROJ_EINVAL;
+    } else if (t.kc != 0) {
+        return PROJ_EINVAL;
+    }
     return PROJ_OK;
 }
 
 proj_tactic_t default_tactic(int N, int K, int bin, int num_cus) {
     // The rule the measured table follows on MI355X: the IEEE weight stream
-    // for 1-2 rows, MFMA from an LDS-transposed weight tile up to 32 rows,
-    // register-fed MFMA tiles above.
+    // for 1-2 rows, MFMA from an LDS-transposed weight tile up to 4 rows, and
+    // above that the shared-tile MFMA kernel, with K split so that each
+    // workgroup holds about one 128-row group (2 workgroups per compute unit).
     proj_tactic_t t{};
     if (num_cus < 1) num_cus = 256;
-    (void)N;
     if (bin <= 2) {
         t.kernel = PROJ_KERNEL_STREAM;
         t.bcap = bin;
@@ -134,21 +153,26 @@ proj_tactic_t default_tactic(int N, int K, int bin, int num_cus) {
         while (stream_lds_bytes(K, t) > 80 * 1024 && t.split < 16) ++t.split;
         return t;
     }
-    if (bin <= 32) {
+    if (bin <= 4) {
         t.kernel = PROJ_KERNEL_MFMA_LDS;
-        t.bcap = bin <= 16 ? 16 : 32;
-        t.rows = bin <= 8 ? 1 : 2;
+        t.bcap = 16;
+        t.rows = 1;
         t.waves = 1;
-        t.wpc = bin <= 8 ? 4 : 0;
+        t.wpc = 4;
         t.split = 1;
         return t;
     }
-    t.kernel = PROJ_KERNEL_MFMA;
-    t.bcap = next_pow2(bin);
-    t.rows = t.bcap >= 256 ? 1 : 4;
-    t.waves = t.bcap >= 256 ? 4 : 2;
-    t.wpc = t.bcap >= 256 ? 4 : 2;
-    t.split = t.bcap >= 256 ? 1 : 2;
+    t.kernel = PROJ_KERNEL_MFMA_XS;
+    t.bcap = std::max(16, next_pow2(bin));
+    t.kc = 128;
+    t.wpc = t.bcap >= 256 ? 1 : 2;
+    t.rows = t.bcap >= 128 ? 4 : 8;
+    t.waves = t.bcap == 16 ? 1 : (t.bcap <= 64 ? 2 : 4);
+    const long blocks = (long)num_cus * t.wpc;
+    const long rows_per_block = std::max(1L, (long)N / blocks);
+    int S = (int)std::min(4L, std::max(1L, (16L * t.rows + rows_per_block / 2) / rows_per_block));
+    while (S > 1 && (K + S - 1) / S < 128) --S;  // keep at least one chunk per slice
+    t.split = S;
     return t;
 }
 

@@ -21,6 +21,7 @@ struct proj_plan_s {
     size_t lds_limit = tp1::kLdsBytes;
     void *ws = nullptr;
     size_t ws_bytes = 0;
+    int *cnt = nullptr;  // fused split-K arrival counters (zeroed)
 };
 
 namespace {
@@ -101,6 +102,23 @@ int proj_plan(int N, int K, const int *batches, int n_batches, unsigned flags,
         p->core.num_cus = cus > 0 ? cus : 256;
         if (lds > 0 && (size_t)lds < p->lds_limit) p->lds_limit = (size_t)lds;
     }
+    if ((flags & PROJ_PLAN_SPLIT_FUSED) && !(flags & PROJ_PLAN_HOST_ONLY)) {
+        // Counters of the fused split-K reduction: zero once here; every
+        // reduction leaves its counter at zero again.
+        void *mem = nullptr;
+        const size_t bytes = (size_t)tp1::kSplitCounters * sizeof(int);
+        if (hipMalloc(&mem, bytes) != hipSuccess) {
+            (void)hipGetLastError();
+            delete p;
+            return PROJ_ENOMEM;
+        }
+        if (hipMemset(mem, 0, bytes) != hipSuccess) {
+            (void)hipFree(mem);
+            delete p;
+            return PROJ_EHIP;
+        }
+        p->cnt = static_cast<int *>(mem);
+    }
     tp1::fill_tactics(p->core);
     // A device with less LDS per workgroup than the table assumes: split K
     // further until the staged x slice fits.
@@ -113,6 +131,7 @@ int proj_plan(int N, int K, const int *batches, int n_batches, unsigned flags,
     }
     rc = alloc_workspace(p, tp1::plan_workspace(p->core));
     if (rc != PROJ_OK) {
+        if (p->cnt) (void)hipFree(p->cnt);
         delete p;
         return rc;
     }
@@ -127,6 +146,13 @@ void proj_free(proj_plan_t *plan) {
         if (hipGetDevice(&cur) == hipSuccess && cur != plan->device)
             (void)hipSetDevice(plan->device);
         (void)hipFree(plan->ws);
+        if (cur >= 0 && cur != plan->device) (void)hipSetDevice(cur);
+    }
+    if (plan->cnt) {
+        int cur = -1;
+        if (hipGetDevice(&cur) == hipSuccess && cur != plan->device)
+            (void)hipSetDevice(plan->device);
+        (void)hipFree(plan->cnt);
         if (cur >= 0 && cur != plan->device) (void)hipSetDevice(cur);
     }
     delete plan;
@@ -158,6 +184,8 @@ int proj_plan_set_tactic(proj_plan_t *plan, int bin, const proj_tactic_t *tactic
     if (tactic->kernel == PROJ_KERNEL_MFMA_LDS &&
         tp1::mfma_lds_tile_bytes(*tactic) > plan->lds_limit)
         return PROJ_EINVAL;
+    if (tactic->kernel == PROJ_KERNEL_MFMA_XS && tp1::mfma_xs_lds_bytes(*tactic) > plan->lds_limit)
+        return PROJ_EINVAL;
     const int rc = alloc_workspace(plan, tp1::tactic_workspace(plan->core.N, plan->core.K, *tactic));
     if (rc != PROJ_OK) return rc;
     plan->core.tactics[i] = *tactic;
@@ -168,9 +196,14 @@ int proj_plan_kernel_name(const proj_plan_t *plan, int B, char *buf, size_t len)
     if (!plan || !buf || len == 0) return PROJ_EINVAL;
     const int i = tp1::bin_index(plan->core, B);
     if (i < 0) return PROJ_EBATCH;
-    return tp1::kernel_name(plan->core.K, plan->core.tactics[i], buf, len) == 0
-               ? PROJ_OK
-               : PROJ_EINVAL;
+    tp1::LaunchShape sh{plan->core.N, plan->core.K, B, nullptr, plan->core.K, nullptr, nullptr,
+                        nullptr, plan->cnt, plan->core.num_cus};
+    if (plan->core.flags & PROJ_PLAN_HOST_ONLY) {
+        // no device counters; name what a device plan would launch
+        static int fake;
+        if (plan->core.flags & PROJ_PLAN_SPLIT_FUSED) sh.cnt = &fake;
+    }
+    return tp1::kernel_name(sh, plan->core.tactics[i], buf, len) == 0 ? PROJ_OK : PROJ_EINVAL;
 }
 
 size_t proj_plan_workspace_bytes(const proj_plan_t *plan) {
@@ -209,6 +242,7 @@ int proj_run(const proj_plan_t *plan, int B, const void *x, long ldx, const void
                         static_cast<const uint16_t *>(W),
                         static_cast<uint16_t *>(y),
                         static_cast<float *>(plan->ws),
+                        plan->cnt,
                         c.num_cus};
     const hipError_t e = tp1::launch_projection(sh, t, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return PROJ_EHIP;

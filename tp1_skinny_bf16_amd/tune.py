@@ -21,8 +21,8 @@ import time
 
 import torch
 
-from . import (KERNEL_IDS, KERNEL_MFMA, KERNEL_MFMA_LDS, KERNEL_STREAM, KERNEL_STREAM_DOT2,
-               Plan, ProjError, Tactic)
+from . import (KERNEL_IDS, KERNEL_MFMA, KERNEL_MFMA_LDS, KERNEL_MFMA_XS, KERNEL_STREAM,
+               KERNEL_STREAM_DOT2, Plan, ProjError, Tactic)
 from .timing import gbs, rotation_copies, time_calls
 
 SHAPES = {"dsa": (14560, 7168), "oproj": (7168, 12288), "kda": (49376, 7168)}
@@ -57,6 +57,13 @@ def candidates(bin_: int, full: bool = False):
         for rows, split, waves, wpc in itertools.product(
                 (1, 2), (1, 2), (1, 2, 3, 4), (0, 2, 4, 6, 8, 12)):
             out.append(Tactic(KERNEL_MFMA_LDS, bc, split, rows, waves, wpc))
+    bc = max(16, next_pow2(bin_))
+    xs = {16: ((4, 1, 128), (8, 1, 128), (8, 1, 256), (16, 1, 128)),
+          32: ((4, 1, 128), (4, 2, 128), (8, 2, 128), (8, 2, 256)),
+          64: ((4, 1, 128), (4, 2, 128), (4, 4, 128), (8, 2, 128), (8, 2, 256)),
+          128: ((4, 2, 128), (4, 4, 128)), 256: ((4, 4, 128), (2, 4, 128))}[bc]
+    for (rows, waves, kc), split, wpc in itertools.product(xs, (1, 2, 3, 4), (1, 2)):
+        out.append(Tactic(KERNEL_MFMA_XS, bc, split, rows, waves, wpc, kc))
     return out
 
 
@@ -65,7 +72,8 @@ def _key(res):
     return (res["us"], t["split"] > 1, t["split"], t["rows"])
 
 
-def measure(N: int, K: int, bins, reps: int = 40, log=None, full: bool = False):
+def measure(N: int, K: int, bins, reps: int = 40, log=None, full: bool = False,
+            fused_split: bool = False):
     dev = torch.device("cuda:0")
     g = torch.Generator(device=dev)
     g.manual_seed(7)
@@ -73,8 +81,8 @@ def measure(N: int, K: int, bins, reps: int = 40, log=None, full: bool = False):
     copies = rotation_copies(W0)
     bmax = max(bins)
     x = torch.randn((bmax, K), generator=g, device=dev).to(torch.bfloat16)
-    plan = Plan(N, K, bins)
-    result = {"N": N, "K": K, "copies": len(copies), "bins": {}}
+    plan = Plan(N, K, bins, fused_split=fused_split)
+    result = {"N": N, "K": K, "copies": len(copies), "bins": {}, "fused_split": fused_split}
     for b in bins:
         y = torch.empty((b, N), dtype=torch.bfloat16, device=dev)
         xb = x[:b]
@@ -124,10 +132,10 @@ def table_rows(result) -> str:
         t = r["chosen"]["tactic"]
         k = {"stream": "PROJ_KERNEL_STREAM", "mfma": "PROJ_KERNEL_MFMA",
              "stream_dot2": "PROJ_KERNEL_STREAM_DOT2",
-             "mfma_lds": "PROJ_KERNEL_MFMA_LDS"}[t["kernel"]]
+             "mfma_lds": "PROJ_KERNEL_MFMA_LDS", "mfma_xs": "PROJ_KERNEL_MFMA_XS"}[t["kernel"]]
         lines.append(f"    {{{result['N']}, {result['K']}, {b}, {{{k}, {t['bcap']}, {t['split']}, "
-                     f"{t['rows']}, {t['waves']}, {t['wpc']}}}}},  // {r['chosen']['us']} us, "
-                     f"{r['GBps']} GB/s")
+                     f"{t['rows']}, {t['waves']}, {t['wpc']}, {t.get('kc', 0)}}}}},  // "
+                     f"{r['chosen']['us']} us, {r['GBps']} GB/s")
     return "\n".join(lines)
 
 
@@ -163,7 +171,7 @@ def summarize(paths) -> str:
     for (N, K) in sorted({(n, k) for n, k, _ in chosen}):
         bins = sorted(b for n, k, b in chosen if (n, k) == (N, K))
         lines += [f"## {N} x {K}", "",
-                  "| bin | chosen kernel | tactic (bcap, split, rows, waves, wpc) | us | GB/s "
+                  "| bin | chosen kernel | tactic (bcap, split, rows, waves, wpc, kc) | us | GB/s "
                   "| best stream us | best MFMA us | candidates |",
                   "|---|---|---|---|---|---|---|---|"]
         cross = None
@@ -173,7 +181,7 @@ def summarize(paths) -> str:
             if cross is None and t["kernel"].startswith("mfma"):
                 cross = b
             lines.append(f"| {b} | `{r['chosen']['kernel']}` | {t['bcap']}, {t['split']}, {t['rows']}, "
-                         f"{t['waves']}, {t['wpc']} | {r['chosen']['us']} | {r['GBps']} | "
+                         f"{t['waves']}, {t['wpc']}, {t.get('kc', 0)} | {r['chosen']['us']} | {r['GBps']} | "
                          f"{r.get('best_stream_us')} | {r.get('best_mfma_us')} | {r['n_candidates']} |")
         lines += ["", f"Crossover (first bin whose best tactic is an MFMA kernel): {cross}", ""]
     return "\n".join(lines)
@@ -192,6 +200,8 @@ def main():
     ap.add_argument("--bins", default="1,2,4,8,16,32,64,128,256")
     ap.add_argument("--reps", type=int, default=40)
     ap.add_argument("--full", action="store_true")
+    ap.add_argument("--fused-split", action="store_true",
+                    help="measure with the in-kernel split-K reduction")
     ap.add_argument("--out", required=True)
     a = ap.parse_args()
     bins = [int(v) for v in a.bins.split(",")]
@@ -199,7 +209,8 @@ def main():
     t0 = time.time()
     for sh in a.shape:
         N, K = SHAPES[sh] if sh in SHAPES else (int(v) for v in sh.split("x"))
-        res = measure(N, K, bins, a.reps, log=lambda m: print(m, flush=True), full=a.full)
+        res = measure(N, K, bins, a.reps, log=lambda m: print(m, flush=True), full=a.full,
+                      fused_split=a.fused_split)
         allres.append(res)
         print(table_rows(res), flush=True)
         print(f"crossover (first MFMA bin) for {N}x{K}: {res['crossover']}  "

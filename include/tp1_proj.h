@@ -93,7 +93,9 @@ enum proj_kernel {
  *            tiles must fit the LDS: waves * 2 * bcap/16 * rows KB <= 160)
  *   wpc    : STREAM: waves per compute unit the grid is sized for
  *            MFMA:   0 = one wave per N range (grid from N), else as STREAM
- *   kc     : MFMA_XS: K chunk staged per step (128 or 256); 0 elsewhere
+ *   kc     : MFMA_XS: K chunk staged per step (128, 256 or 512); 0 elsewhere
+ *   depth  : MFMA_XS: chunks loaded ahead of the one being multiplied (1 or
+ *            2); 0 elsewhere
  */
 typedef struct proj_tactic {
     int kernel;
@@ -103,6 +105,7 @@ typedef struct proj_tactic {
     int waves;
     int wpc;
     int kc;
+    int depth;
 } proj_tactic_t;
 
 typedef struct proj_plan_s proj_plan_t;

@@ -102,16 +102,18 @@ def candidate_tactics(N: int, K: int, bin_: int):
                 for split in (1, 2):
                     for waves, wpc in ((4, 0), (2, 3), (1, 8), (3, 4)):
                         out.append(tp.Tactic(tp.KERNEL_MFMA_LDS, bc, split, rows, waves, wpc))
-    for bc, shapes in ((16, ((4, 1, 128), (8, 1, 256), (16, 1, 128))),
-                       (32, ((4, 1, 128), (4, 2, 128), (8, 2, 256))),
-                       (64, ((4, 1, 128), (4, 4, 128), (8, 2, 256))),
-                       (128, ((4, 2, 128), (4, 4, 128))), (256, ((4, 4, 128), (2, 4, 128)))):
+    for bc, shapes in ((16, ((4, 1, 128, 1), (4, 1, 256, 2), (4, 1, 512, 1), (8, 1, 128, 2),
+                             (16, 1, 128, 1))),
+                       (32, ((4, 1, 128, 2), (4, 2, 128, 1), (8, 2, 256, 1))),
+                       (64, ((4, 1, 128, 1), (4, 2, 128, 2), (4, 4, 128, 1), (8, 2, 256, 1))),
+                       (128, ((4, 2, 128, 1), (4, 4, 128, 1))),
+                       (256, ((4, 4, 128, 1), (2, 4, 128, 1)))):
         if bc < bin_:
             continue
-        for (rows, waves, kc) in shapes:
+        for (rows, waves, kc, depth) in shapes:
             for split in (1, 3):
                 for wpc in (1, 2):
-                    out.append(tp.Tactic(tp.KERNEL_MFMA_XS, bc, split, rows, waves, wpc, kc))
+                    out.append(tp.Tactic(tp.KERNEL_MFMA_XS, bc, split, rows, waves, wpc, kc, depth))
     for bc in (16, 32, 64, 128, 256):
         if bc < bin_:
             continue

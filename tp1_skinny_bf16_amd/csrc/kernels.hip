@@ -714,12 +714,12 @@ __global__ __launch_bounds__(256) void mfma_lds_kernel(MfmaArgs a) {
 // group's rows) in LDS once, both with 256- or 512-byte row pieces,
 // and every wave reads its A and B fragments from there: the waves split
 // the tile WM x (4/WM), so each holds (MT/WM) x (NTB*WM/4) accumulator tiles
-// and reuses each fragment across them.  The next chunk is loaded into
-// registers while this one is multiplied; two barriers per chunk.  LDS rows
+// and reuses each fragment across them.  The next one or two chunks are
+// loaded into registers while this one is multiplied; two barriers per chunk.  LDS rows
 // are padded by 16 bytes so the 16 rows of a fragment read fall in distinct
 // banks.
 // ---------------------------------------------------------------------------
-template <int MT, int NTB, int WM, int kXsChunk>
+template <int MT, int NTB, int WM, int kXsChunk, int PD>
 __global__ __launch_bounds__(256) void mfma_xs_kernel(MfmaArgs a) {
     constexpr int kXsPitch = kXsChunk + 8;   // bf16 per LDS row (16 bytes of pad)
     constexpr int WN = 4 / WM;
@@ -761,82 +761,97 @@ __global__ __launch_bounds__(256) void mfma_xs_kernel(MfmaArgs a) {
             a.ws[((size_t)s * a.B + row) * a.N + col] = v;
     };
 
-    u32x4 xr[XV], wr[WV];
-    auto load_chunk = [&](int g, int c) {
-        const int kk = min(c * kXsChunk + pk, klen - 8);
+    // PD register sets: chunks t+1 .. t+PD are in flight while chunk t is
+    // multiplied.
+    u32x4 xr[PD][XV], wr[PD][WV];
+    const int T = Gb * C;
+    if (T == 0) return;  // uniform over the workgroup: no barrier is skipped by part of it
+
+    // Load cursor over (group, chunk); a load past the last step reads the
+    // first 16 bytes of x and of W instead (one cache line each for the whole
+    // grid, never stored), so every round issues the same loads.  The offset,
+    // not the base pointer, is selected: a pointer select becomes a branch.
+    int lt = 0, lg = 0, lc = 0;
+    auto load_chunk = [&](u32x4 (&xx)[XV], u32x4 (&ww)[WV]) {
+        const size_t live = lt < T ? 1 : 0;
+        const int kk = min(lc * kXsChunk + pk, klen - 8);
 #pragma unroll
         for (int i = 0; i < XV; ++i) {
             const int b = min(i * RPS + prow, a.B - 1);
-            xr[i] = load_cached(a.x + (size_t)b * a.ldx + k0 + kk);
+            xx[i] = load_cached(a.x + live * ((size_t)b * a.ldx + k0 + kk));
         }
 #pragma unroll
         for (int i = 0; i < WV; ++i) {
-            const int r = min(g * GR + i * RPS + prow, rows - 1);
-            wr[i] = load_stream(a.W + (size_t)(row0 + r) * a.K + k0 + kk);
+            const int r = min(lg * GR + i * RPS + prow, rows - 1);
+            ww[i] = load_stream(a.W + live * ((size_t)(row0 + r) * a.K + k0 + kk));
         }
+        ++lt;
+        if (++lc == C) { lc = 0; ++lg; }
     };
-    auto store_chunk = [&](int c) {
+    auto store_chunk = [&](const u32x4 (&xx)[XV], const u32x4 (&ww)[WV], int c) {
         const bool dead = c * kXsChunk + pk >= klen;   // past the slice
 #pragma unroll
         for (int i = 0; i < XV; ++i)
-            *reinterpret_cast<u32x4 *>(xt + (i * RPS + prow) * kXsPitch + pk) = xr[i];
+            *reinterpret_cast<u32x4 *>(xt + (i * RPS + prow) * kXsPitch + pk) = xx[i];
 #pragma unroll
         for (int i = 0; i < WV; ++i)
             *reinterpret_cast<u32x4 *>(wt + (i * RPS + prow) * kXsPitch + pk) =
-                dead ? u32x4{0u, 0u, 0u, 0u} : wr[i];
+                dead ? u32x4{0u, 0u, 0u, 0u} : ww[i];
     };
 
-    const int T = Gb * C;
-    if (T == 0) return;  // uniform over the workgroup: no barrier is skipped by part of it
     f32x4 acc[MTW][NTW];
 #pragma unroll
     for (int m = 0; m < MTW; ++m)
 #pragma unroll
         for (int n = 0; n < NTW; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    load_chunk(0, 0);
+#pragma unroll
+    for (int p = 0; p < PD; ++p) load_chunk(xr[p], wr[p]);
     int g = 0, c = 0;
-    for (int t = 0; t < T; ++t) {
-        __syncthreads();                 // every wave is done with the previous tiles
-        store_chunk(c);
-        __syncthreads();                 // tiles of step t visible
-        const int ng = (c + 1 == C) ? g + 1 : g;
-        const int nc = (c + 1 == C) ? 0 : c + 1;
-        if (t + 1 < T) load_chunk(ng, nc);   // uniform: next chunk into registers
+    for (int t0 = 0; t0 < T; t0 += PD) {
 #pragma unroll
-        for (int j = 0; j < kXsChunk / 32; ++j) {
-            u32x4 bf[NTW];
+        for (int p = 0; p < PD; ++p) {
+            if (t0 + p < T) {                // uniform
+                __syncthreads();             // every wave is done with the previous tiles
+                store_chunk(xr[p], wr[p], c);
+                __syncthreads();             // tiles of this step visible
+                load_chunk(xr[p], wr[p]);    // the step PD ahead into this set
+                __builtin_amdgcn_sched_barrier(0);   // all loads issue before the MFMAs
 #pragma unroll
-            for (int n = 0; n < NTW; ++n)
-                bf[n] = *reinterpret_cast<const u32x4 *>(
-                    wt + ((wn * NTW + n) * 16 + lrow) * kXsPitch + j * 32 + lgrp * 8);
+                for (int j = 0; j < kXsChunk / 32; ++j) {
+                    u32x4 bf[NTW];
 #pragma unroll
-            for (int m = 0; m < MTW; ++m) {
-                const u32x4 af = *reinterpret_cast<const u32x4 *>(
-                    xt + ((wm * MTW + m) * 16 + lrow) * kXsPitch + j * 32 + lgrp * 8);
+                    for (int n = 0; n < NTW; ++n)
+                        bf[n] = *reinterpret_cast<const u32x4 *>(
+                            wt + ((wn * NTW + n) * 16 + lrow) * kXsPitch + j * 32 + lgrp * 8);
 #pragma unroll
-                for (int n = 0; n < NTW; ++n)
-                    acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        __builtin_bit_cast(bf16x8_t, af), __builtin_bit_cast(bf16x8_t, bf[n]),
-                        acc[m][n], 0, 0, 0);
+                    for (int m = 0; m < MTW; ++m) {
+                        const u32x4 af = *reinterpret_cast<const u32x4 *>(
+                            xt + ((wm * MTW + m) * 16 + lrow) * kXsPitch + j * 32 + lgrp * 8);
+#pragma unroll
+                        for (int n = 0; n < NTW; ++n)
+                            acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                __builtin_bit_cast(bf16x8_t, af),
+                                __builtin_bit_cast(bf16x8_t, bf[n]), acc[m][n], 0, 0, 0);
+                    }
+                }
+                if (c == C - 1) {
+#pragma unroll
+                    for (int m = 0; m < MTW; ++m)
+#pragma unroll
+                        for (int n = 0; n < NTW; ++n) {
+                            const int r = g * GR + (wn * NTW + n) * 16 + lrow;
+#pragma unroll
+                            for (int v = 0; v < 4; ++v) {
+                                const int b = (wm * MTW + m) * 16 + lgrp * 4 + v;
+                                if (b < a.B && r < rows) store_out(b, row0 + r, acc[m][n][v]);
+                            }
+                            acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+                        }
+                }
+                if (++c == C) { c = 0; ++g; }
             }
         }
-        if (c == C - 1) {
-#pragma unroll
-            for (int m = 0; m < MTW; ++m)
-#pragma unroll
-                for (int n = 0; n < NTW; ++n) {
-                    const int r = g * GR + (wn * NTW + n) * 16 + lrow;
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) {
-                        const int b = (wm * MTW + m) * 16 + lgrp * 4 + v;
-                        if (b < a.B && r < rows) store_out(b, row0 + r, acc[m][n][v]);
-                    }
-                    acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-                }
-        }
-        g = ng;
-        c = nc;
     }
     if (a.S > 1 && a.cnt) splitk_fixup(a.ws, a.y, a.cnt, a.N, a.B, row0, rows);
 }
@@ -1009,7 +1024,7 @@ hipError_t launch_mfma_lds(const LaunchShape &sh, const proj_tactic_t &t, hipStr
     return hipErrorInvalidValue;
 }
 
-template <int MT, int NTB, int WM, int KC>
+template <int MT, int NTB, int WM, int KC, int PD>
 hipError_t launch_mfma_xs_inst(const LaunchShape &sh, const proj_tactic_t &t,
                                hipStream_t stream) {
     const int ks = slice_len(sh.K, t);
@@ -1019,23 +1034,24 @@ hipError_t launch_mfma_xs_inst(const LaunchShape &sh, const proj_tactic_t &t,
     static size_t lds_allowed = 64 * 1024;
     if (lds > lds_allowed) {
         hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void *>(&mfma_xs_kernel<MT, NTB, WM, KC>),
+            reinterpret_cast<const void *>(&mfma_xs_kernel<MT, NTB, WM, KC, PD>),
             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
         lds_allowed = lds;
     }
     MfmaArgs a{sh.x, sh.ldx, sh.W, sh.y, sh.ws, fused_counters(sh, g, S), sh.N, sh.K, sh.B,
                ks, S};
-    hipLaunchKernelGGL((mfma_xs_kernel<MT, NTB, WM, KC>), dim3((unsigned)g, S), dim3(256), lds,
+    hipLaunchKernelGGL((mfma_xs_kernel<MT, NTB, WM, KC, PD>), dim3((unsigned)g, S), dim3(256), lds,
                        stream, a);
     return hipGetLastError();
 }
 
 hipError_t launch_mfma_xs(const LaunchShape &sh, const proj_tactic_t &t, hipStream_t st) {
-    // rows = N tiles per group (NTB); waves = waves along M (WM); kc = K chunk
-#define TP1_XS_CASE(BC, NTB, WM, KC) \
-    if (t.bcap == BC && t.rows == NTB && t.waves == WM && t.kc == KC) \
-        return launch_mfma_xs_inst<BC / 16, NTB, WM, KC>(sh, t, st);
+    // rows = N tiles per group (NTB); waves = waves along M (WM); kc = K
+    // chunk; depth = chunks in flight
+#define TP1_XS_CASE(BC, NTB, WM, KC, PD) \
+    if (t.bcap == BC && t.rows == NTB && t.waves == WM && t.kc == KC && t.depth == PD) \
+        return launch_mfma_xs_inst<BC / 16, NTB, WM, KC, PD>(sh, t, st);
     TP1_XS_INSTANCES(TP1_XS_CASE)
 #undef TP1_XS_CASE
     return hipErrorInvalidValue;
@@ -1108,8 +1124,8 @@ int kernel_name(const LaunchShape &sh, const proj_tactic_t &t, char *buf, size_t
         n = snprintf(buf, len, "mfma_lds_kernel<%d, %d>%s", t.bcap / 16, t.rows,
                      split ? "+splitk_reduce" : "");
     else if (t.kernel == PROJ_KERNEL_MFMA_XS)
-        n = snprintf(buf, len, "mfma_xs_kernel<%d, %d, %d, %d>%s", t.bcap / 16, t.rows, t.waves,
-                     t.kc, split ? "+splitk_reduce" : "");
+        n = snprintf(buf, len, "mfma_xs_kernel<%d, %d, %d, %d, %d>%s", t.bcap / 16, t.rows,
+                     t.waves, t.kc, t.depth, split ? "+splitk_reduce" : "");
     else
         n = snprintf(buf, len, "mfma_kernel<%d, %d, %d>%s", t.bcap / 16, t.rows,
                      mfma_ring(t.bcap / 16, t.rows), split ? "+splitk_reduce" : "");

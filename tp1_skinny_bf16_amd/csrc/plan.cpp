@@ -59,8 +59,9 @@ bool tactic_instance_exists(const proj_tactic_t &t) {
     if (t.kernel == PROJ_KERNEL_MFMA_LDS)
         return (t.bcap == 16 || t.bcap == 32) && (t.rows == 1 || t.rows == 2);
     if (t.kernel == PROJ_KERNEL_MFMA_XS) {
-#define TP1_XS_MATCH(BC, NTB, WM, KC) \
-        if (t.bcap == BC && t.rows == NTB && t.waves == WM && t.kc == KC) return true;
+#define TP1_XS_MATCH(BC, NTB, WM, KC, PD) \
+        if (t.bcap == BC && t.rows == NTB && t.waves == WM && t.kc == KC && t.depth == PD) \
+            return true;
         TP1_XS_INSTANCES(TP1_XS_MATCH)
 #undef TP1_XS_MATCH
         return false;
@@ -130,7 +131,7 @@ int check_tactic(int N, int K, int bin, const proj_tactic_t &t) {
     if (t.kernel == PROJ_KERNEL_MFMA_XS) {
         if (t.wpc < 1 || t.wpc > 2) return PROJ_EINVAL;
         if (mfma_xs_lds_bytes(t) > kLdsBytes) return PROJ_EINVAL;
-    } else if (t.kc != 0) {
+    } else if (t.kc != 0 || t.depth != 0) {
         return PROJ_EINVAL;
     }
     return PROJ_OK;
@@ -165,6 +166,7 @@ proj_tactic_t default_tactic(int N, int K, int bin, int num_cus) {
     t.kernel = PROJ_KERNEL_MFMA_XS;
     t.bcap = std::max(16, next_pow2(bin));
     t.kc = 128;
+    t.depth = 1;
     t.wpc = t.bcap >= 256 ? 1 : 2;
     t.rows = t.bcap >= 128 ? 4 : 8;
     t.waves = t.bcap == 16 ? 1 : (t.bcap <= 64 ? 2 : 4);

@@ -25,13 +25,14 @@ struct PlanCore {
     int num_cus = 256;                        // compute units of the device
 };
 
-// The compiled shared-tile MFMA instances: X(bcap, rows, waves, kc).
-#define TP1_XS_INSTANCES(X)                                                       \
-    X(16, 4, 1, 128) X(16, 8, 1, 128) X(16, 8, 1, 256) X(16, 16, 1, 128)          \
-    X(32, 4, 1, 128) X(32, 4, 2, 128) X(32, 8, 2, 128) X(32, 8, 2, 256)           \
-    X(64, 4, 1, 128) X(64, 4, 2, 128) X(64, 4, 4, 128) X(64, 8, 2, 128)           \
-    X(64, 8, 2, 256) X(128, 4, 2, 128) X(128, 4, 4, 128) X(256, 4, 4, 128)        \
-    X(256, 2, 4, 128)
+// The compiled shared-tile MFMA instances: X(bcap, rows, waves, kc, depth).
+#define TP1_XS_INSTANCES(X)                                                          \
+    X(16, 4, 1, 128, 1) X(16, 4, 1, 128, 2) X(16, 4, 1, 256, 2) X(16, 4, 1, 512, 1)  \
+    X(16, 8, 1, 128, 1) X(16, 8, 1, 128, 2) X(16, 8, 1, 256, 1) X(16, 16, 1, 128, 1) \
+    X(32, 4, 1, 128, 1) X(32, 4, 1, 128, 2) X(32, 4, 2, 128, 1) X(32, 8, 2, 128, 1)  \
+    X(32, 8, 2, 256, 1) X(64, 4, 1, 128, 1) X(64, 4, 2, 128, 1) X(64, 4, 2, 128, 2)  \
+    X(64, 4, 4, 128, 1) X(64, 8, 2, 128, 1) X(64, 8, 2, 256, 1) X(128, 4, 2, 128, 1) \
+    X(128, 4, 4, 128, 1) X(256, 4, 4, 128, 1) X(256, 2, 4, 128, 1)
 
 // LDS bytes of an MFMA_XS tactic (x and W chunk tiles, 16 bytes of row pad).
 size_t mfma_xs_lds_bytes(const proj_tactic_t &t);

@@ -55,11 +55,14 @@ enum proj_kernel {
     PROJ_KERNEL_MFMA_LDS = 4, /* MFMA tiles fed from a per-wave LDS tile that
                                the weight reaches with 1 KB row loads
                                (bcap 16 or 32, rows 1 or 2)              */
-    PROJ_KERNEL_MFMA_XS = 5  /* large batches: x and W chunk tiles staged
-                               once per workgroup in LDS and shared by its
-                               4 waves (bcap 64/128/256; rows = N tiles
-                               per group, 2 or 4; waves = waves along the
-                               batch, 1/2/4; wpc = workgroups per CU)    */
+    PROJ_KERNEL_MFMA_XS = 5, /* x and W chunk tiles staged once per
+                               workgroup in LDS and shared by its 4 waves
+                               (bcap 16..256; rows = 16-row N tiles per
+                               group; waves = waves along the batch, 1/2/4;
+                               wpc = workgroups per CU, 1 or 2)          */
+    PROJ_KERNEL_MFMA_PIPE = 6 /* as MFMA_XS, but the tiles are loaded
+                               directly into a ring of `depth` LDS stages,
+                               depth-1 chunks ahead of the multiply      */
 };
 
 /* Plan flags. */
@@ -93,9 +96,11 @@ enum proj_kernel {
  *            tiles must fit the LDS: waves * 2 * bcap/16 * rows KB <= 160)
  *   wpc    : STREAM: waves per compute unit the grid is sized for
  *            MFMA:   0 = one wave per N range (grid from N), else as STREAM
- *   kc     : MFMA_XS: K chunk staged per step (128, 256 or 512); 0 elsewhere
- *   depth  : MFMA_XS: chunks loaded ahead of the one being multiplied (1 or
- *            2); 0 elsewhere
+ *   kc     : MFMA_XS, MFMA_PIPE: K chunk staged per step (32..512);
+ *            0 elsewhere
+ *   depth  : MFMA_XS: chunks loaded into registers ahead of the one being
+ *            multiplied (1 or 2); MFMA_PIPE: LDS stages of the ring (3 or
+ *            4); 0 elsewhere
  */
 typedef struct proj_tactic {
     int kernel;

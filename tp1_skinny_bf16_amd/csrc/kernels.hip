@@ -18,6 +18,10 @@
 //                  the A operand (batch rows) and W as the B operand (output
 //                  columns), both loaded straight into registers in operand
 //                  layout, FP32 accumulators.
+//   mfma_xs_kernel / mfma_pipe_kernel  a workgroup shares one x tile and
+//                  one weight tile per K chunk in LDS; the pipe variant
+//                  fills a ring of LDS stages with direct-to-LDS loads several
+//                  chunks ahead.
 //   splitk_reduce  when K is split across workgroups: sums the FP32 slices
 //                  in the fixed order s = 0..S-1 and rounds to BF16 (no
 //                  atomics, so results are bitwise reproducible).
@@ -857,6 +861,204 @@ __global__ __launch_bounds__(256) void mfma_xs_kernel(MfmaArgs a) {
 }
 
 // ---------------------------------------------------------------------------
+// Pipelined shared-tile MFMA kernel.
+//
+// Same work split as mfma_xs_kernel (a workgroup owns a row range of one K
+// slice; its four waves step together through (group, chunk) pairs, sharing
+// the chunk's x tile [16*MT][KC] and weight tile [16*NTB][KC] in LDS), but
+// the tiles are loaded straight into LDS with global_load_lds_dwordx4 into a
+// ring of D stages, D-1 chunks ahead of the one being multiplied, so the
+// loads in flight do not hold registers and no wave copies data into LDS.
+// One barrier per chunk.
+//
+// LDS layout of a stage: rows of KC/8 16-byte pieces, x rows first, then
+// weight rows; piece p of row r sits at position (p + (r >> SH)) mod (KC/8)
+// of its row, a rotation that puts the 16 rows of an MFMA fragment read in
+// 16 distinct bank groups without padding.  One load instruction fills 1 KB
+// of consecutive positions (64 lanes x 16 bytes), so each lane loads the
+// global piece that lands in its position.  Pieces past the slice end, batch
+// rows past B and weight rows past the workgroup's rows load 16 zero bytes
+// instead (zero x or weight pieces add nothing; the rows' outputs are never
+// stored).
+//
+// The direct-to-LDS loads are issued from inline assembly, so the compiler
+// does not track them: the wait for a stage is an explicit vmcnt wait for
+// all but the (D-2) younger stages' loads of this wave (vector loads return
+// in order), then a barrier for the other waves' pieces.
+// ---------------------------------------------------------------------------
+__device__ __align__(16) uint16_t kZeroPiece[8];
+
+// LDS byte address of a shared-memory pointer (what M0 and ds_* take).
+__device__ __forceinline__ uint32_t lds_address(const void *p) {
+    return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void *)p;
+}
+
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+// 16 bytes per lane from src into LDS at m0 + 16 * lane (m0 uniform).  A
+// load that reads M0 right after a scalar write of it needs one wait state.
+__device__ __forceinline__ void lds_load16_stream(const void *src, uint32_t m0) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
+                 :
+                 : "v"(src), "s"(m0)
+                 : "memory", "m0");
+}
+__device__ __forceinline__ void lds_load16_cached(const void *src, uint32_t m0) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src), "s"(m0)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// s_waitcnt vmcnt(N) leaving the other counters alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+template <int MT, int NTB, int WM, int KC, int D>
+__global__ __launch_bounds__(256) void mfma_pipe_kernel(MfmaArgs a) {
+    constexpr int WN = 4 / WM;
+    constexpr int MTW = MT / WM;                 // x tiles per wave
+    constexpr int NTW = NTB / WN;                // weight tiles per wave
+    constexpr int XR = 16 * MT;                  // x rows per stage
+    constexpr int GR = 16 * NTB;                 // weight rows per group
+    constexpr int PP = KC / 8;                   // 16-byte pieces per row
+    constexpr int SH = PP >= 16 ? 0 : (PP == 8 ? 1 : 2);
+    constexpr int STAGE = (XR + GR) * PP * 16;   // bytes per stage
+    constexpr int NB = (XR + GR) * PP / 64;      // 1 KB load blocks per stage
+    constexpr int XB = XR * PP / 64;             // of which x blocks
+    constexpr int NI = NB / 4;                   // blocks per wave per stage
+    static_assert(PP == 4 || PP == 8 || PP % 16 == 0, "chunk width");
+    static_assert(PP <= 64, "a row piece fits one load instruction");
+    static_assert(NB % 4 == 0 && (XR * PP) % 64 == 0, "blocks split over four waves");
+    static_assert(MT % WM == 0 && NTB % WN == 0, "tile split");
+    static_assert(D >= 2 && NI * (D - 2) <= 63, "loads in flight");
+    extern __shared__ __align__(16) uint16_t pipe_lds[];
+    const char *lds = reinterpret_cast<const char *>(pipe_lds);
+    const uint32_t lds0 = uniform((int)lds_address(pipe_lds));
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = uniform(tid >> 6);
+    const int wm = wave / WN, wn = wave - (wave / WN) * WN;
+    const int s = blockIdx.y;
+    const int k0 = s * a.ks;
+    const int klen = min(a.K - k0, a.ks);
+    const int row0 = (int)((long)a.N * blockIdx.x / gridDim.x);
+    const int rows = (int)((long)a.N * (blockIdx.x + 1) / gridDim.x) - row0;
+    const int C = (klen + KC - 1) / KC;
+    const int Gb = (rows + GR - 1) / GR;
+    const int T = Gb * C;
+    if (T == 0) return;  // uniform over the workgroup
+    const int lrow = lane & 15, lgrp = lane >> 4;
+
+    // This lane's piece of each of the wave's load blocks: stage row r and
+    // piece p (its K offset within the chunk is 8 * p).
+    int lr[NI], lpk[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+        const int slot = (i * 4 + wave) * 64 + lane;
+        const int r = slot / PP;
+        lr[i] = r;
+        lpk[i] = (((slot % PP) - (r >> SH)) & (PP - 1)) * 8;
+    }
+
+    int it = 0, ig = 0, ic = 0;  // the next step to load
+    auto issue = [&]() {
+        const uint32_t st = lds0 + (uint32_t)((it % D) * STAGE);
+        const bool live = it < T;  // uniform; past the end only zeros load
+#pragma unroll
+        for (int i = 0; i < NI; ++i) {
+            const int bi = i * 4 + wave;
+            const int k = ic * KC + lpk[i];
+            const uint32_t m0 = st + (uint32_t)bi * 1024u;
+            if (bi < XB) {
+                const int b = lr[i];
+                const bool ok = live && k < klen && b < a.B;
+                const uint16_t *src =
+                    ok ? a.x + (size_t)b * a.ldx + k0 + k : kZeroPiece;
+                lds_load16_cached(src, m0);
+            } else {
+                const int r = ig * GR + lr[i] - XR;
+                const bool ok = live && k < klen && r < rows;
+                const uint16_t *src =
+                    ok ? a.W + (size_t)(row0 + r) * a.K + k0 + k : kZeroPiece;
+                lds_load16_stream(src, m0);
+            }
+        }
+        ++it;
+        if (++ic == C) { ic = 0; ++ig; }
+    };
+
+    auto store_out = [&](int row, int col, float v) {
+        if (a.S == 1)
+            a.y[(size_t)row * a.N + col] = to_bf16(v);
+        else
+            a.ws[((size_t)s * a.B + row) * a.N + col] = v;
+    };
+
+    f32x4 acc[MTW][NTW];
+#pragma unroll
+    for (int m = 0; m < MTW; ++m)
+#pragma unroll
+        for (int n = 0; n < NTW; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+    for (int p = 0; p < D - 1; ++p) issue();
+    int g = 0, c = 0;
+    for (int t = 0; t < T; ++t) {
+        wait_vmcnt<NI * (D - 2)>();  // this wave's pieces of step t are in LDS
+        __syncthreads();             // everyone's are; stage t-1 is free
+        issue();                     // step t + D - 1 into the freed stage
+        const char *stg = lds + (t % D) * STAGE;
+#pragma unroll
+        for (int j = 0; j < KC / 32; ++j) {
+            const int p = j * 4 + lgrp;
+            u32x4 bf[NTW];
+#pragma unroll
+            for (int n = 0; n < NTW; ++n) {
+                const int r = XR + (wn * NTW + n) * 16 + lrow;
+                bf[n] = *reinterpret_cast<const u32x4 *>(
+                    stg + (r * PP + ((p + (r >> SH)) & (PP - 1))) * 16);
+            }
+#pragma unroll
+            for (int m = 0; m < MTW; ++m) {
+                const int r = (wm * MTW + m) * 16 + lrow;
+                const u32x4 af = *reinterpret_cast<const u32x4 *>(
+                    stg + (r * PP + ((p + (r >> SH)) & (PP - 1))) * 16);
+#pragma unroll
+                for (int n = 0; n < NTW; ++n)
+                    acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        __builtin_bit_cast(bf16x8_t, af), __builtin_bit_cast(bf16x8_t, bf[n]),
+                        acc[m][n], 0, 0, 0);
+            }
+        }
+        if (c == C - 1) {
+#pragma unroll
+            for (int m = 0; m < MTW; ++m)
+#pragma unroll
+                for (int n = 0; n < NTW; ++n) {
+                    const int r = g * GR + (wn * NTW + n) * 16 + lrow;
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) {
+                        const int b = (wm * MTW + m) * 16 + lgrp * 4 + v;
+                        if (b < a.B && r < rows) store_out(b, row0 + r, acc[m][n][v]);
+                    }
+                    acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+                }
+        }
+        if (++c == C) { c = 0; ++g; }
+    }
+    // The ring's last loads (zeros past the end) land before the workgroup
+    // ends; no wave leaves LDS writes in flight.
+    wait_vmcnt<0>();
+    if (a.S > 1 && a.cnt) splitk_fixup(a.ws, a.y, a.cnt, a.N, a.B, row0, rows);
+}
+
+// ---------------------------------------------------------------------------
 // Fixed-order split-K reduction: y[i] = bf16( sum_{s=0}^{S-1} ws[s][i] ).
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void splitk_reduce(const float *ws, uint16_t *y,
@@ -916,7 +1118,7 @@ long grid_x(const LaunchShape &sh, const proj_tactic_t &t) {
     if (t.kernel == PROJ_KERNEL_STREAM || t.kernel == PROJ_KERNEL_STREAM_DOT2) {
         const int nw = std::min(t.waves, kStreamMaxWaves);
         g = (long)sh.num_cus * t.wpc / (nw * (long)S);
-    } else if (t.kernel == PROJ_KERNEL_MFMA_XS) {
+    } else if (t.kernel == PROJ_KERNEL_MFMA_XS || t.kernel == PROJ_KERNEL_MFMA_PIPE) {
         g = (long)sh.num_cus * std::max(1, t.wpc) / S;
     } else {
         const int nw = std::min(t.waves, 4);
@@ -1057,6 +1259,39 @@ hipError_t launch_mfma_xs(const LaunchShape &sh, const proj_tactic_t &t, hipStre
     return hipErrorInvalidValue;
 }
 
+template <int MT, int NTB, int WM, int KC, int D>
+hipError_t launch_mfma_pipe_inst(const LaunchShape &sh, const proj_tactic_t &t,
+                                 hipStream_t stream) {
+    const int ks = slice_len(sh.K, t);
+    const int S = slice_count(sh.K, t);
+    const long g = grid_x(sh, t);
+    const size_t lds = mfma_pipe_lds_bytes(t);
+    static size_t lds_allowed = 64 * 1024;
+    if (lds > lds_allowed) {
+        hipError_t e = hipFuncSetAttribute(
+            reinterpret_cast<const void *>(&mfma_pipe_kernel<MT, NTB, WM, KC, D>),
+            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+        lds_allowed = lds;
+    }
+    MfmaArgs a{sh.x, sh.ldx, sh.W, sh.y, sh.ws, fused_counters(sh, g, S), sh.N, sh.K, sh.B,
+               ks, S};
+    hipLaunchKernelGGL((mfma_pipe_kernel<MT, NTB, WM, KC, D>), dim3((unsigned)g, S), dim3(256),
+                       lds, stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_mfma_pipe(const LaunchShape &sh, const proj_tactic_t &t, hipStream_t st) {
+    // rows = N tiles per group; waves = waves along M; kc = K chunk; depth =
+    // LDS stages
+#define TP1_PIPE_CASE(BC, NTB, WM, KC, D) \
+    if (t.bcap == BC && t.rows == NTB && t.waves == WM && t.kc == KC && t.depth == D) \
+        return launch_mfma_pipe_inst<BC / 16, NTB, WM, KC, D>(sh, t, st);
+    TP1_PIPE_INSTANCES(TP1_PIPE_CASE)
+#undef TP1_PIPE_CASE
+    return hipErrorInvalidValue;
+}
+
 hipError_t launch_stream(const LaunchShape &sh, const proj_tactic_t &t,
                          hipStream_t st) {
     const bool d2 = t.kernel == PROJ_KERNEL_STREAM_DOT2;
@@ -1097,6 +1332,8 @@ hipError_t launch_projection(const LaunchShape &sh, const proj_tactic_t &t,
         e = launch_mfma_lds(sh, t, stream);
     else if (t.kernel == PROJ_KERNEL_MFMA_XS)
         e = launch_mfma_xs(sh, t, stream);
+    else if (t.kernel == PROJ_KERNEL_MFMA_PIPE)
+        e = launch_mfma_pipe(sh, t, stream);
     else
         return hipErrorInvalidValue;
     if (e != hipSuccess) return e;
@@ -1125,6 +1362,9 @@ int kernel_name(const LaunchShape &sh, const proj_tactic_t &t, char *buf, size_t
                      split ? "+splitk_reduce" : "");
     else if (t.kernel == PROJ_KERNEL_MFMA_XS)
         n = snprintf(buf, len, "mfma_xs_kernel<%d, %d, %d, %d, %d>%s", t.bcap / 16, t.rows,
+                     t.waves, t.kc, t.depth, split ? "+splitk_reduce" : "");
+    else if (t.kernel == PROJ_KERNEL_MFMA_PIPE)
+        n = snprintf(buf, len, "mfma_pipe_kernel<%d, %d, %d, %d, %d>%s", t.bcap / 16, t.rows,
                      t.waves, t.kc, t.depth, split ? "+splitk_reduce" : "");
     else
         n = snprintf(buf, len, "mfma_kernel<%d, %d, %d>%s", t.bcap / 16, t.rows,

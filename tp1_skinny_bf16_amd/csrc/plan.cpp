@@ -63,6 +63,10 @@ bool tactic_instance_exists(const proj_tactic_t &t) {
         if (t.bcap == BC && t.rows == NTB && t.waves == WM && t.kc == KC && t.depth == PD) \
             return true;
         TP1_XS_INSTANCES(TP1_XS_MATCH)
+        return false;
+    }
+    if (t.kernel == PROJ_KERNEL_MFMA_PIPE) {
+        TP1_PIPE_INSTANCES(TP1_XS_MATCH)
 #undef TP1_XS_MATCH
         return false;
     }
@@ -73,7 +77,9 @@ int slice_len(int K, const proj_tactic_t &t) {
     const int S = std::max(1, t.split);
     // K granularity of a slice: one MFMA step, one shared chunk, or 8
     const int step = t.kernel == PROJ_KERNEL_MFMA ? 32
-                     : (t.kernel == PROJ_KERNEL_MFMA_XS ? std::max(t.kc, 32) : 8);
+                     : (t.kernel == PROJ_KERNEL_MFMA_XS || t.kernel == PROJ_KERNEL_MFMA_PIPE
+                            ? std::max(t.kc, 32)
+                            : 8);
     int ks = ceil_div(K, S);
     ks = ceil_div(ks, step) * step;
     return std::max(ks, step);
@@ -91,6 +97,10 @@ size_t stream_lds_bytes(int K, const proj_tactic_t &t) {
 
 size_t mfma_xs_lds_bytes(const proj_tactic_t &t) {
     return (size_t)(t.bcap + 16 * t.rows) * (size_t)(t.kc + 8) * 2u;
+}
+
+size_t mfma_pipe_lds_bytes(const proj_tactic_t &t) {
+    return (size_t)t.depth * (size_t)(t.bcap + 16 * t.rows) * (size_t)t.kc * 2u;
 }
 
 size_t mfma_lds_tile_bytes(const proj_tactic_t &t) {
@@ -131,6 +141,9 @@ int check_tactic(int N, int K, int bin, const proj_tactic_t &t) {
     if (t.kernel == PROJ_KERNEL_MFMA_XS) {
         if (t.wpc < 1 || t.wpc > 2) return PROJ_EINVAL;
         if (mfma_xs_lds_bytes(t) > kLdsBytes) return PROJ_EINVAL;
+    } else if (t.kernel == PROJ_KERNEL_MFMA_PIPE) {
+        if (t.wpc < 1 || t.wpc > 2) return PROJ_EINVAL;
+        if (mfma_pipe_lds_bytes(t) > kLdsBytes) return PROJ_EINVAL;
     } else if (t.kc != 0 || t.depth != 0) {
         return PROJ_EINVAL;
     }
@@ -139,9 +152,11 @@ int check_tactic(int N, int K, int bin, const proj_tactic_t &t) {
 
 proj_tactic_t default_tactic(int N, int K, int bin, int num_cus) {
     // The rule the measured table follows on MI355X: the IEEE weight stream
-    // for 1-2 rows, MFMA from an LDS-transposed weight tile up to 4 rows, and
-    // above that the shared-tile MFMA kernel, with K split so that each
-    // workgroup holds about one 128-row group (2 workgroups per compute unit).
+    // for 1-2 rows, the pipelined shared-tile MFMA kernel up to 32 rows (one
+    // workgroup per compute unit, K split until a workgroup holds about one
+    // 16*rows-row group), and above that the shared-tile MFMA kernel with K
+    // split so that each workgroup holds about one 128-row group (2
+    // workgroups per compute unit).
     proj_tactic_t t{};
     if (num_cus < 1) num_cus = 256;
     if (bin <= 2) {
@@ -154,13 +169,19 @@ proj_tactic_t default_tactic(int N, int K, int bin, int num_cus) {
         while (stream_lds_bytes(K, t) > 80 * 1024 && t.split < 16) ++t.split;
         return t;
     }
-    if (bin <= 4) {
-        t.kernel = PROJ_KERNEL_MFMA_LDS;
-        t.bcap = 16;
-        t.rows = 1;
-        t.waves = 1;
-        t.wpc = 4;
-        t.split = 1;
+    if (bin <= 32) {
+        t.kernel = PROJ_KERNEL_MFMA_PIPE;
+        t.bcap = bin <= 16 ? 16 : 32;
+        t.rows = bin <= 16 ? 4 : 8;
+        t.waves = bin <= 16 ? 1 : 2;
+        t.kc = 128;
+        t.depth = bin <= 16 ? 4 : 3;
+        t.wpc = 1;
+        const long group = 16L * t.rows;
+        const long rows_per_block = std::max(1L, (long)N / num_cus);
+        int S = (int)std::min(4L, (group + rows_per_block - 1) / rows_per_block);
+        while (S > 1 && (K + S - 1) / S < 128) --S;  // keep at least one chunk per slice
+        t.split = std::max(1, S);
         return t;
     }
     t.kernel = PROJ_KERNEL_MFMA_XS;

@@ -21,8 +21,8 @@ import time
 
 import torch
 
-from . import (KERNEL_IDS, KERNEL_MFMA, KERNEL_MFMA_LDS, KERNEL_MFMA_XS, KERNEL_STREAM,
-               KERNEL_STREAM_DOT2, Plan, ProjError, Tactic)
+from . import (KERNEL_IDS, KERNEL_MFMA, KERNEL_MFMA_LDS, KERNEL_MFMA_PIPE, KERNEL_MFMA_XS,
+               KERNEL_STREAM, KERNEL_STREAM_DOT2, Plan, ProjError, Tactic)
 from .timing import gbs, rotation_copies, time_calls
 
 SHAPES = {"dsa": (14560, 7168), "oproj": (7168, 12288), "kda": (49376, 7168)}
@@ -66,6 +66,14 @@ def candidates(bin_: int, full: bool = False):
           128: ((4, 2, 128, 1), (4, 4, 128, 1)), 256: ((4, 4, 128, 1), (2, 4, 128, 1))}[bc]
     for (rows, waves, kc, depth), split, wpc in itertools.product(xs, (1, 2, 3, 4), (1, 2)):
         out.append(Tactic(KERNEL_MFMA_XS, bc, split, rows, waves, wpc, kc, depth))
+    pipe = {16: ((4, 1, 128, 3), (4, 1, 128, 4), (4, 1, 128, 6), (4, 1, 256, 3), (8, 1, 128, 3),
+                 (8, 1, 128, 4)),
+            32: ((4, 1, 128, 4), (4, 1, 128, 6), (4, 2, 64, 8), (8, 2, 128, 3)),
+            64: ((4, 2, 64, 8), (4, 2, 128, 4), (4, 4, 64, 8), (8, 2, 64, 4), (8, 2, 64, 6)),
+            128: ((4, 4, 64, 6), (4, 4, 32, 12), (8, 4, 64, 4), (8, 4, 32, 8)),
+            256: ((4, 4, 32, 7), (4, 4, 64, 3), (8, 4, 32, 6), (8, 4, 64, 3))}[bc]
+    for (rows, waves, kc, depth), split, wpc in itertools.product(pipe, (1, 2, 3, 4), (1, 2)):
+        out.append(Tactic(KERNEL_MFMA_PIPE, bc, split, rows, waves, wpc, kc, depth))
     return out
 
 
@@ -118,7 +126,7 @@ def measure(N: int, K: int, bins, reps: int = 40, log=None, full: bool = False,
         chosen = near[0]
         nbytes = 2 * N * K + 2 * b * K + 2 * b * N
         result["bins"][b] = {"chosen": chosen, "GBps": round(gbs(nbytes, chosen["us"]), 1),
-                             "top": rows[:8], "n_candidates": len(rows)}
+                             "top": rows[:8], "all": rows, "n_candidates": len(rows)}
         best_stream = min((r for r in rows if r["tactic"]["kernel"].startswith("stream")),
                           key=lambda r: r["us"], default=None)
         best_mfma = min((r for r in rows if r["tactic"]["kernel"].startswith("mfma")),
@@ -143,7 +151,8 @@ def table_rows(result) -> str:
         t = r["chosen"]["tactic"]
         k = {"stream": "PROJ_KERNEL_STREAM", "mfma": "PROJ_KERNEL_MFMA",
              "stream_dot2": "PROJ_KERNEL_STREAM_DOT2",
-             "mfma_lds": "PROJ_KERNEL_MFMA_LDS", "mfma_xs": "PROJ_KERNEL_MFMA_XS"}[t["kernel"]]
+             "mfma_lds": "PROJ_KERNEL_MFMA_LDS", "mfma_xs": "PROJ_KERNEL_MFMA_XS",
+             "mfma_pipe": "PROJ_KERNEL_MFMA_PIPE"}[t["kernel"]]
         lines.append(f"    {{{result['N']}, {result['K']}, {b}, {{{k}, {t['bcap']}, {t['split']}, "
                      f"{t['rows']}, {t['waves']}, {t['wpc']}, {t.get('kc', 0)}, "
                      f"{t.get('depth', 0)}}}}},  // "

@@ -36,7 +36,8 @@ def _args():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--report", default=None, help="write the all-config report here")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="wall time of the bounded oracle sample (whole steps)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy 5 times, the known-size "
                          "reference that scales FETCH_SIZE / WRITE_SIZE counters")
@@ -145,8 +146,13 @@ def measured_traffic(kernel: str):
         data = json.load(f)
     if data.get("source_hash") != profile_summary.source_hash():
         return None
-    entry = data.get("kernels", {}).get(kernel.split("+")[0])
-    return int(entry["traffic"]) if entry else None
+    total = 0
+    for part in kernel.split("+"):   # a split-K call is the main kernel + splitk_reduce
+        entry = data.get("kernels", {}).get(part)
+        if not entry:
+            return None
+        total += entry["traffic"]
+    return int(total)
 
 
 def cpu_baseline(args, cfg, t, wl):
@@ -160,7 +166,7 @@ def cpu_baseline(args, cfg, t, wl):
         for B in cfg.batches:
             oracle.proj(xb[:B], wb, threads=threads)
         reps += 1
-        if time.perf_counter() - t0 >= args.cpu_seconds or reps >= 50:
+        if time.perf_counter() - t0 >= args.cpu_seconds or reps >= 1000:
             break
     el = time.perf_counter() - t0
     step_bytes = sum(wl.algorithmic_bytes(B, cfg.N, cfg.K) for B in cfg.batches)

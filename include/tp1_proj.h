@@ -99,8 +99,11 @@ enum proj_kernel {
  *   kc     : MFMA_XS, MFMA_PIPE: K chunk staged per step (32..512);
  *            0 elsewhere
  *   depth  : MFMA_XS: chunks loaded into registers ahead of the one being
- *            multiplied (1 or 2); MFMA_PIPE: LDS stages of the ring (3 or
- *            4); 0 elsewhere
+ *            multiplied (1 or 2); MFMA_PIPE: LDS stages of the ring (3..12);
+ *            0 elsewhere
+ *   kw     : MFMA_PIPE: waves along K (1, 2 or 4): the 4 waves of a
+ *            workgroup split each chunk's K steps kw ways and add their
+ *            partial tiles in LDS in a fixed order; 0 elsewhere
  */
 typedef struct proj_tactic {
     int kernel;
@@ -111,6 +114,7 @@ typedef struct proj_tactic {
     int wpc;
     int kc;
     int depth;
+    int kw;
 } proj_tactic_t;
 
 typedef struct proj_plan_s proj_plan_t;

@@ -56,7 +56,7 @@ class _Tactic(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int), ("bcap", ctypes.c_int),
                 ("split", ctypes.c_int), ("rows", ctypes.c_int),
                 ("waves", ctypes.c_int), ("wpc", ctypes.c_int), ("kc", ctypes.c_int),
-                ("depth", ctypes.c_int)]
+                ("depth", ctypes.c_int), ("kw", ctypes.c_int)]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -69,6 +69,7 @@ class Tactic:
     wpc: int
     kc: int = 0
     depth: int = 0
+    kw: int = 0
 
     @property
     def kernel_name(self) -> str:
@@ -81,7 +82,7 @@ class Tactic:
 
     def _c(self) -> _Tactic:
         return _Tactic(self.kernel, self.bcap, self.split, self.rows, self.waves,
-                       self.wpc, self.kc, self.depth)
+                       self.wpc, self.kc, self.depth, self.kw)
 
 
 _LIB = None
@@ -197,7 +198,8 @@ class Plan:
         b = ctypes.c_int()
         _check(_lib().proj_plan_tactic(self._h, int(B), ctypes.byref(t), ctypes.byref(b)),
                f"proj_plan_tactic(B={B})")
-        return Tactic(t.kernel, t.bcap, t.split, t.rows, t.waves, t.wpc, t.kc, t.depth), b.value
+        return (Tactic(t.kernel, t.bcap, t.split, t.rows, t.waves, t.wpc, t.kc, t.depth, t.kw),
+                b.value)
 
     def kernel_name(self, B: int) -> str:
         """Kernel instance(s) proj_run launches for batch B (profiler names)."""

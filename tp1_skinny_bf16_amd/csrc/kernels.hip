@@ -918,11 +918,13 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-template <int MT, int NTB, int WM, int KC, int D>
+template <int MT, int NTB, int WM, int WK, int KC, int D>
 __global__ __launch_bounds__(256) void mfma_pipe_kernel(MfmaArgs a) {
-    constexpr int WN = 4 / WM;
+    static_assert(WM * WK <= 4 && 4 % (WM * WK) == 0, "four waves");
+    constexpr int WN = 4 / (WM * WK);
     constexpr int MTW = MT / WM;                 // x tiles per wave
     constexpr int NTW = NTB / WN;                // weight tiles per wave
+    constexpr int JW = KC / 32 / WK;             // 32-wide K steps per wave per chunk
     constexpr int XR = 16 * MT;                  // x rows per stage
     constexpr int GR = 16 * NTB;                 // weight rows per group
     constexpr int PP = KC / 8;                   // 16-byte pieces per row
@@ -936,6 +938,7 @@ __global__ __launch_bounds__(256) void mfma_pipe_kernel(MfmaArgs a) {
     static_assert(NB % 4 == 0 && (XR * PP) % 64 == 0, "blocks split over four waves");
     static_assert(MT % WM == 0 && NTB % WN == 0, "tile split");
     static_assert(D >= 2 && NI * (D - 2) <= 63, "loads in flight");
+    static_assert(JW * WK * 32 == KC, "K steps split over the waves along K");
     extern __shared__ __align__(16) uint16_t pipe_lds[];
     const char *lds = reinterpret_cast<const char *>(pipe_lds);
     const uint32_t lds0 = uniform((int)lds_address(pipe_lds));
@@ -943,7 +946,9 @@ __global__ __launch_bounds__(256) void mfma_pipe_kernel(MfmaArgs a) {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = uniform(tid >> 6);
-    const int wm = wave / WN, wn = wave - (wave / WN) * WN;
+    const int wk = wave / (WM * WN);             // which K steps of a chunk
+    const int wmn = wave - wk * (WM * WN);
+    const int wm = wmn / WN, wn = wmn - (wmn / WN) * WN;
     const int s = blockIdx.y;
     const int k0 = s * a.ks;
     const int klen = min(a.K - k0, a.ks);
@@ -1015,8 +1020,8 @@ __global__ __launch_bounds__(256) void mfma_pipe_kernel(MfmaArgs a) {
         issue();                     // step t + D - 1 into the freed stage
         const char *stg = lds + (t % D) * STAGE;
 #pragma unroll
-        for (int j = 0; j < KC / 32; ++j) {
-            const int p = j * 4 + lgrp;
+        for (int jj = 0; jj < JW; ++jj) {
+            const int p = (jj * WK + wk) * 4 + lgrp;
             u32x4 bf[NTW];
 #pragma unroll
             for (int n = 0; n < NTW; ++n) {
@@ -1037,6 +1042,30 @@ __global__ __launch_bounds__(256) void mfma_pipe_kernel(MfmaArgs a) {
             }
         }
         if (c == C - 1) {
+            if constexpr (WK > 1) {
+                // Waves along K leave their partial tiles after the ring;
+                // the first one adds them in the fixed order wk = 1..WK-1.
+                f32x4 *part = reinterpret_cast<f32x4 *>(pipe_lds + D * STAGE / 2);
+                if (wk > 0) {
+#pragma unroll
+                    for (int m = 0; m < MTW; ++m)
+#pragma unroll
+                        for (int n = 0; n < NTW; ++n)
+                            part[(((wk - 1) * WM * WN + wmn) * MTW * NTW + m * NTW + n) * 64 +
+                                 lane] = acc[m][n];
+                }
+                __syncthreads();
+                if (wk == 0) {
+#pragma unroll
+                    for (int q = 1; q < WK; ++q)
+#pragma unroll
+                        for (int m = 0; m < MTW; ++m)
+#pragma unroll
+                            for (int n = 0; n < NTW; ++n)
+                                acc[m][n] += part[(((q - 1) * WM * WN + wmn) * MTW * NTW +
+                                                   m * NTW + n) * 64 + lane];
+                }
+            }
 #pragma unroll
             for (int m = 0; m < MTW; ++m)
 #pragma unroll
@@ -1045,7 +1074,7 @@ __global__ __launch_bounds__(256) void mfma_pipe_kernel(MfmaArgs a) {
 #pragma unroll
                     for (int v = 0; v < 4; ++v) {
                         const int b = (wm * MTW + m) * 16 + lgrp * 4 + v;
-                        if (b < a.B && r < rows) store_out(b, row0 + r, acc[m][n][v]);
+                        if (wk == 0 && b < a.B && r < rows) store_out(b, row0 + r, acc[m][n][v]);
                     }
                     acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
                 }
@@ -1259,7 +1288,7 @@ hipError_t launch_mfma_xs(const LaunchShape &sh, const proj_tactic_t &t, hipStre
     return hipErrorInvalidValue;
 }
 
-template <int MT, int NTB, int WM, int KC, int D>
+template <int MT, int NTB, int WM, int WK, int KC, int D>
 hipError_t launch_mfma_pipe_inst(const LaunchShape &sh, const proj_tactic_t &t,
                                  hipStream_t stream) {
     const int ks = slice_len(sh.K, t);
@@ -1269,24 +1298,25 @@ hipError_t launch_mfma_pipe_inst(const LaunchShape &sh, const proj_tactic_t &t,
     static size_t lds_allowed = 64 * 1024;
     if (lds > lds_allowed) {
         hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void *>(&mfma_pipe_kernel<MT, NTB, WM, KC, D>),
+            reinterpret_cast<const void *>(&mfma_pipe_kernel<MT, NTB, WM, WK, KC, D>),
             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
         lds_allowed = lds;
     }
     MfmaArgs a{sh.x, sh.ldx, sh.W, sh.y, sh.ws, fused_counters(sh, g, S), sh.N, sh.K, sh.B,
                ks, S};
-    hipLaunchKernelGGL((mfma_pipe_kernel<MT, NTB, WM, KC, D>), dim3((unsigned)g, S), dim3(256),
+    hipLaunchKernelGGL((mfma_pipe_kernel<MT, NTB, WM, WK, KC, D>), dim3((unsigned)g, S), dim3(256),
                        lds, stream, a);
     return hipGetLastError();
 }
 
 hipError_t launch_mfma_pipe(const LaunchShape &sh, const proj_tactic_t &t, hipStream_t st) {
-    // rows = N tiles per group; waves = waves along M; kc = K chunk; depth =
-    // LDS stages
-#define TP1_PIPE_CASE(BC, NTB, WM, KC, D) \
-    if (t.bcap == BC && t.rows == NTB && t.waves == WM && t.kc == KC && t.depth == D) \
-        return launch_mfma_pipe_inst<BC / 16, NTB, WM, KC, D>(sh, t, st);
+    // rows = N tiles per group; waves = waves along M; kw = waves along K;
+    // kc = K chunk; depth = LDS stages
+#define TP1_PIPE_CASE(BC, NTB, WM, WK, KC, D)                                         \
+    if (t.bcap == BC && t.rows == NTB && t.waves == WM && t.kw == WK && t.kc == KC && \
+        t.depth == D)                                                                 \
+        return launch_mfma_pipe_inst<BC / 16, NTB, WM, WK, KC, D>(sh, t, st);
     TP1_PIPE_INSTANCES(TP1_PIPE_CASE)
 #undef TP1_PIPE_CASE
     return hipErrorInvalidValue;
@@ -1364,8 +1394,8 @@ int kernel_name(const LaunchShape &sh, const proj_tactic_t &t, char *buf, size_t
         n = snprintf(buf, len, "mfma_xs_kernel<%d, %d, %d, %d, %d>%s", t.bcap / 16, t.rows,
                      t.waves, t.kc, t.depth, split ? "+splitk_reduce" : "");
     else if (t.kernel == PROJ_KERNEL_MFMA_PIPE)
-        n = snprintf(buf, len, "mfma_pipe_kernel<%d, %d, %d, %d, %d>%s", t.bcap / 16, t.rows,
-                     t.waves, t.kc, t.depth, split ? "+splitk_reduce" : "");
+        n = snprintf(buf, len, "mfma_pipe_kernel<%d, %d, %d, %d, %d, %d>%s", t.bcap / 16,
+                     t.rows, t.waves, t.kw, t.kc, t.depth, split ? "+splitk_reduce" : "");
     else
         n = snprintf(buf, len, "mfma_kernel<%d, %d, %d>%s", t.bcap / 16, t.rows,
                      mfma_ring(t.bcap / 16, t.rows), split ? "+splitk_reduce" : "");

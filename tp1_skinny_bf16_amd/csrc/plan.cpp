@@ -63,11 +63,16 @@ bool tactic_instance_exists(const proj_tactic_t &t) {
         if (t.bcap == BC && t.rows == NTB && t.waves == WM && t.kc == KC && t.depth == PD) \
             return true;
         TP1_XS_INSTANCES(TP1_XS_MATCH)
+#undef TP1_XS_MATCH
         return false;
     }
     if (t.kernel == PROJ_KERNEL_MFMA_PIPE) {
-        TP1_PIPE_INSTANCES(TP1_XS_MATCH)
-#undef TP1_XS_MATCH
+#define TP1_PIPE_MATCH(BC, NTB, WM, WK, KC, D)                                           \
+        if (t.bcap == BC && t.rows == NTB && t.waves == WM && t.kw == WK && t.kc == KC && \
+            t.depth == D)                                                                 \
+            return true;
+        TP1_PIPE_INSTANCES(TP1_PIPE_MATCH)
+#undef TP1_PIPE_MATCH
         return false;
     }
     return false;
@@ -100,7 +105,11 @@ size_t mfma_xs_lds_bytes(const proj_tactic_t &t) {
 }
 
 size_t mfma_pipe_lds_bytes(const proj_tactic_t &t) {
-    return (size_t)t.depth * (size_t)(t.bcap + 16 * t.rows) * (size_t)t.kc * 2u;
+    const size_t ring = (size_t)t.depth * (size_t)(t.bcap + 16 * t.rows) * (size_t)t.kc * 2u;
+    const size_t parts = t.kw > 1 ? (size_t)(t.kw - 1) * (size_t)(t.bcap / 16) *
+                                        (size_t)t.rows * 1024u
+                                  : 0;
+    return ring + parts;
 }
 
 size_t mfma_lds_tile_bytes(const proj_tactic_t &t) {
@@ -147,6 +156,7 @@ int check_tactic(int N, int K, int bin, const proj_tactic_t &t) {
     } else if (t.kc != 0 || t.depth != 0) {
         return PROJ_EINVAL;
     }
+    if (t.kernel != PROJ_KERNEL_MFMA_PIPE && t.kw != 0) return PROJ_EINVAL;
     return PROJ_OK;
 }
 
@@ -176,6 +186,7 @@ proj_tactic_t default_tactic(int N, int K, int bin, int num_cus) {
         t.waves = bin <= 16 ? 1 : 2;
         t.kc = 128;
         t.depth = bin <= 16 ? 4 : 3;
+        t.kw = 1;
         t.wpc = 1;
         const long group = 16L * t.rows;
         const long rows_per_block = std::max(1L, (long)N / num_cus);

@@ -66,14 +66,17 @@ def candidates(bin_: int, full: bool = False):
           128: ((4, 2, 128, 1), (4, 4, 128, 1)), 256: ((4, 4, 128, 1), (2, 4, 128, 1))}[bc]
     for (rows, waves, kc, depth), split, wpc in itertools.product(xs, (1, 2, 3, 4), (1, 2)):
         out.append(Tactic(KERNEL_MFMA_XS, bc, split, rows, waves, wpc, kc, depth))
-    pipe = {16: ((4, 1, 128, 3), (4, 1, 128, 4), (4, 1, 128, 6), (4, 1, 256, 3), (8, 1, 128, 3),
-                 (8, 1, 128, 4)),
-            32: ((4, 1, 128, 4), (4, 1, 128, 6), (4, 2, 64, 8), (8, 2, 128, 3)),
-            64: ((4, 2, 64, 8), (4, 2, 128, 4), (4, 4, 64, 8), (8, 2, 64, 4), (8, 2, 64, 6)),
-            128: ((4, 4, 64, 6), (4, 4, 32, 12), (8, 4, 64, 4), (8, 4, 32, 8)),
-            256: ((4, 4, 32, 7), (4, 4, 64, 3), (8, 4, 32, 6), (8, 4, 64, 3))}[bc]
-    for (rows, waves, kc, depth), split, wpc in itertools.product(pipe, (1, 2, 3, 4), (1, 2)):
-        out.append(Tactic(KERNEL_MFMA_PIPE, bc, split, rows, waves, wpc, kc, depth))
+    pipe = {16: ((4, 1, 1, 128, 3), (4, 1, 1, 128, 4), (4, 1, 1, 128, 6), (4, 1, 1, 256, 3),
+                 (8, 1, 1, 128, 3), (8, 1, 1, 128, 4), (2, 1, 2, 256, 6), (2, 1, 2, 256, 4),
+                 (2, 1, 2, 128, 8), (1, 1, 4, 256, 4), (1, 1, 4, 256, 6)),
+            32: ((4, 1, 1, 128, 4), (4, 1, 1, 128, 6), (4, 2, 1, 64, 8), (8, 2, 1, 128, 3),
+                 (2, 1, 2, 256, 4), (2, 2, 1, 256, 4)),
+            64: ((4, 2, 1, 64, 8), (4, 2, 1, 128, 4), (4, 4, 1, 64, 8), (8, 2, 1, 64, 4),
+                 (8, 2, 1, 64, 6)),
+            128: ((4, 4, 1, 64, 6), (4, 4, 1, 32, 12), (8, 4, 1, 64, 4), (8, 4, 1, 32, 8)),
+            256: ((4, 4, 1, 32, 7), (4, 4, 1, 64, 3), (8, 4, 1, 32, 6), (8, 4, 1, 64, 3))}[bc]
+    for (rows, waves, kw, kc, depth), split, wpc in itertools.product(pipe, (1, 2, 3, 4), (1, 2)):
+        out.append(Tactic(KERNEL_MFMA_PIPE, bc, split, rows, waves, wpc, kc, depth, kw))
     return out
 
 
@@ -148,14 +151,16 @@ def measure(N: int, K: int, bins, reps: int = 40, log=None, full: bool = False,
 def table_rows(result) -> str:
     lines = []
     for b, r in result["bins"].items():
-        t = r["chosen"]["tactic"]
+        t = dict(r["chosen"]["tactic"])
+        if t["kernel"] == "mfma_pipe" and not t.get("kw"):
+            t["kw"] = 1  # measured before the field existed: one wave along K
         k = {"stream": "PROJ_KERNEL_STREAM", "mfma": "PROJ_KERNEL_MFMA",
              "stream_dot2": "PROJ_KERNEL_STREAM_DOT2",
              "mfma_lds": "PROJ_KERNEL_MFMA_LDS", "mfma_xs": "PROJ_KERNEL_MFMA_XS",
              "mfma_pipe": "PROJ_KERNEL_MFMA_PIPE"}[t["kernel"]]
         lines.append(f"    {{{result['N']}, {result['K']}, {b}, {{{k}, {t['bcap']}, {t['split']}, "
                      f"{t['rows']}, {t['waves']}, {t['wpc']}, {t.get('kc', 0)}, "
-                     f"{t.get('depth', 0)}}}}},  // "
+                     f"{t.get('depth', 0)}, {t.get('kw', 0)}}}}},  // "
                      f"{r['chosen']['us']} us, {r['GBps']} GB/s")
     return "\n".join(lines)
 
@@ -192,7 +197,8 @@ def summarize(paths) -> str:
     for (N, K) in sorted({(n, k) for n, k, _ in chosen}):
         bins = sorted(b for n, k, b in chosen if (n, k) == (N, K))
         lines += [f"## {N} x {K}", "",
-                  "| bin | chosen kernel | tactic (bcap, split, rows, waves, wpc, kc, depth) | us | GB/s "
+                  "| bin | chosen kernel | tactic (bcap, split, rows, waves, wpc, kc, depth, kw) | us "
+                  "| GB/s "
                   "| best stream us | best MFMA us | candidates |",
                   "|---|---|---|---|---|---|---|---|"]
         cross = None
@@ -202,7 +208,8 @@ def summarize(paths) -> str:
             if cross is None and t["kernel"].startswith("mfma"):
                 cross = b
             lines.append(f"| {b} | `{r['chosen']['kernel']}` | {t['bcap']}, {t['split']}, {t['rows']}, "
-                         f"{t['waves']}, {t['wpc']}, {t.get('kc', 0)}, {t.get('depth', 0)} | "
+                         f"{t['waves']}, {t['wpc']}, {t.get('kc', 0)}, {t.get('depth', 0)}, "
+                         f"{t.get('kw', 0)} | "
                          f"{r['chosen']['us']} | {r['GBps']} | "
                          f"{r.get('best_stream_us')} | {r.get('best_mfma_us')} | {r['n_candidates']} |")
         lines += ["", f"Crossover (first bin whose best tactic is an MFMA kernel): {cross}", ""]

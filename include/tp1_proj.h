@@ -101,9 +101,10 @@ enum proj_kernel {
  *   depth  : MFMA_XS: chunks loaded into registers ahead of the one being
  *            multiplied (1 or 2); MFMA_PIPE: LDS stages of the ring (3..12);
  *            0 elsewhere
- *   kw     : MFMA_PIPE: waves along K (1, 2 or 4): the 4 waves of a
+ *   kw     : MFMA_PIPE: waves along K (1, 2 or 4): the waves of a
  *            workgroup split each chunk's K steps kw ways and add their
  *            partial tiles in LDS in a fixed order; 0 elsewhere
+ *   nw     : MFMA_PIPE: waves per workgroup (4 or 8); 0 elsewhere
  */
 typedef struct proj_tactic {
     int kernel;
@@ -115,6 +116,7 @@ typedef struct proj_tactic {
     int kc;
     int depth;
     int kw;
+    int nw;
 } proj_tactic_t;
 
 typedef struct proj_plan_s proj_plan_t;

@@ -114,23 +114,31 @@ def candidate_tactics(N: int, K: int, bin_: int):
             for split in (1, 3):
                 for wpc in (1, 2):
                     out.append(tp.Tactic(tp.KERNEL_MFMA_XS, bc, split, rows, waves, wpc, kc, depth))
-    pipe = {16: ((4, 1, 1, 128, 3), (4, 1, 1, 128, 4), (4, 1, 1, 128, 6), (4, 1, 1, 256, 3),
-                 (8, 1, 1, 128, 3), (8, 1, 1, 128, 4), (2, 1, 2, 256, 6), (2, 1, 2, 256, 4),
-                 (2, 1, 2, 128, 8), (1, 1, 4, 256, 4), (1, 1, 4, 256, 6)),
-            32: ((4, 1, 1, 128, 4), (4, 1, 1, 128, 6), (4, 2, 1, 64, 8), (8, 2, 1, 128, 3),
-                 (2, 1, 2, 256, 4), (2, 2, 1, 256, 4)),
-            64: ((4, 2, 1, 64, 8), (4, 2, 1, 128, 4), (4, 4, 1, 64, 8), (8, 2, 1, 64, 4),
-                 (8, 2, 1, 64, 6)),
-            128: ((4, 4, 1, 64, 6), (4, 4, 1, 32, 12), (8, 4, 1, 64, 4), (8, 4, 1, 32, 8)),
-            256: ((4, 4, 1, 32, 7), (4, 4, 1, 64, 3), (8, 4, 1, 32, 6), (8, 4, 1, 64, 3))}
+    pipe = {16: ((4, 1, 1, 128, 3, 4), (4, 1, 1, 128, 4, 4), (4, 1, 1, 128, 6, 4),
+                 (4, 1, 1, 256, 3, 4), (8, 1, 1, 128, 3, 4), (8, 1, 1, 128, 4, 4),
+                 (2, 1, 2, 256, 6, 4), (2, 1, 2, 256, 4, 4), (2, 1, 2, 128, 8, 4),
+                 (1, 1, 4, 256, 4, 4), (1, 1, 4, 256, 6, 4), (8, 1, 1, 256, 2, 8),
+                 (4, 1, 2, 256, 3, 8)),
+            32: ((4, 1, 1, 128, 4, 4), (4, 1, 1, 128, 6, 4), (4, 2, 1, 64, 8, 4),
+                 (8, 2, 1, 128, 3, 4), (2, 1, 2, 256, 4, 4), (2, 2, 1, 256, 4, 4),
+                 (8, 2, 1, 128, 3, 8)),
+            64: ((4, 2, 1, 64, 8, 4), (4, 2, 1, 128, 4, 4), (4, 4, 1, 64, 8, 4),
+                 (8, 2, 1, 64, 4, 4), (8, 2, 1, 64, 6, 4), (16, 2, 1, 64, 3, 8),
+                 (8, 2, 1, 128, 3, 8), (16, 1, 1, 64, 3, 8), (8, 4, 1, 128, 3, 8)),
+            128: ((4, 4, 1, 64, 6, 4), (4, 4, 1, 32, 12, 4), (8, 4, 1, 64, 4, 4),
+                  (8, 4, 1, 32, 8, 4), (16, 2, 1, 64, 3, 8), (8, 2, 1, 64, 4, 8),
+                  (16, 4, 1, 32, 4, 8)),
+            256: ((4, 4, 1, 32, 7, 4), (4, 4, 1, 64, 3, 4), (8, 4, 1, 32, 6, 4),
+                  (8, 4, 1, 64, 3, 4), (16, 4, 1, 32, 4, 8),
+                  (8, 4, 1, 64, 3, 8), (8, 8, 1, 64, 3, 8))}
     for bc, shapes in pipe.items():
         if bc < bin_:
             continue
-        for (rows, waves, kw, kc, depth) in shapes:
+        for (rows, waves, kw, kc, depth, nw) in shapes:
             for split in (1, 3):
                 for wpc in (1, 2):
                     out.append(tp.Tactic(tp.KERNEL_MFMA_PIPE, bc, split, rows, waves, wpc, kc,
-                                         depth, kw))
+                                         depth, kw, nw))
     for bc in (16, 32, 64, 128, 256):
         if bc < bin_:
             continue

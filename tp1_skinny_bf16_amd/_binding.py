@@ -56,7 +56,7 @@ class _Tactic(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int), ("bcap", ctypes.c_int),
                 ("split", ctypes.c_int), ("rows", ctypes.c_int),
                 ("waves", ctypes.c_int), ("wpc", ctypes.c_int), ("kc", ctypes.c_int),
-                ("depth", ctypes.c_int), ("kw", ctypes.c_int)]
+                ("depth", ctypes.c_int), ("kw", ctypes.c_int), ("nw", ctypes.c_int)]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -70,6 +70,7 @@ class Tactic:
     kc: int = 0
     depth: int = 0
     kw: int = 0
+    nw: int = 0
 
     @property
     def kernel_name(self) -> str:
@@ -82,7 +83,7 @@ class Tactic:
 
     def _c(self) -> _Tactic:
         return _Tactic(self.kernel, self.bcap, self.split, self.rows, self.waves,
-                       self.wpc, self.kc, self.depth, self.kw)
+                       self.wpc, self.kc, self.depth, self.kw, self.nw)
 
 
 _LIB = None
@@ -198,8 +199,8 @@ class Plan:
         b = ctypes.c_int()
         _check(_lib().proj_plan_tactic(self._h, int(B), ctypes.byref(t), ctypes.byref(b)),
                f"proj_plan_tactic(B={B})")
-        return (Tactic(t.kernel, t.bcap, t.split, t.rows, t.waves, t.wpc, t.kc, t.depth, t.kw),
-                b.value)
+        return (Tactic(t.kernel, t.bcap, t.split, t.rows, t.waves, t.wpc, t.kc, t.depth, t.kw,
+                       t.nw), b.value)
 
     def kernel_name(self, B: int) -> str:
         """Kernel instance(s) proj_run launches for batch B (profiler names)."""

@@ -864,7 +864,7 @@ __global__ __launch_bounds__(256) void mfma_xs_kernel(MfmaArgs a) {
 // Pipelined shared-tile MFMA kernel.
 //
 // Same work split as mfma_xs_kernel (a workgroup owns a row range of one K
-// slice; its four waves step together through (group, chunk) pairs, sharing
+// slice; its four or eight waves step together through (group, chunk) pairs, sharing
 // the chunk's x tile [16*MT][KC] and weight tile [16*NTB][KC] in LDS), but
 // the tiles are loaded straight into LDS with global_load_lds_dwordx4 into a
 // ring of D stages, D-1 chunks ahead of the one being multiplied, so the
@@ -918,10 +918,11 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-template <int MT, int NTB, int WM, int WK, int KC, int D>
-__global__ __launch_bounds__(256) void mfma_pipe_kernel(MfmaArgs a) {
-    static_assert(WM * WK <= 4 && 4 % (WM * WK) == 0, "four waves");
-    constexpr int WN = 4 / (WM * WK);
+template <int MT, int NTB, int WM, int WK, int KC, int D, int NWV>
+__global__ __launch_bounds__(NWV * 64) void mfma_pipe_kernel(MfmaArgs a) {
+    static_assert(NWV == 4 || NWV == 8, "four or eight waves");
+    static_assert(WM * WK <= NWV && NWV % (WM * WK) == 0, "wave split");
+    constexpr int WN = NWV / (WM * WK);
     constexpr int MTW = MT / WM;                 // x tiles per wave
     constexpr int NTW = NTB / WN;                // weight tiles per wave
     constexpr int JW = KC / 32 / WK;             // 32-wide K steps per wave per chunk
@@ -932,10 +933,10 @@ __global__ __launch_bounds__(256) void mfma_pipe_kernel(MfmaArgs a) {
     constexpr int STAGE = (XR + GR) * PP * 16;   // bytes per stage
     constexpr int NB = (XR + GR) * PP / 64;      // 1 KB load blocks per stage
     constexpr int XB = XR * PP / 64;             // of which x blocks
-    constexpr int NI = NB / 4;                   // blocks per wave per stage
+    constexpr int NI = NB / NWV;                 // blocks per wave per stage
     static_assert(PP == 4 || PP == 8 || PP % 16 == 0, "chunk width");
     static_assert(PP <= 64, "a row piece fits one load instruction");
-    static_assert(NB % 4 == 0 && (XR * PP) % 64 == 0, "blocks split over four waves");
+    static_assert(NB % NWV == 0 && (XR * PP) % 64 == 0, "blocks split over the waves");
     static_assert(MT % WM == 0 && NTB % WN == 0, "tile split");
     static_assert(D >= 2 && NI * (D - 2) <= 63, "loads in flight");
     static_assert(JW * WK * 32 == KC, "K steps split over the waves along K");
@@ -965,7 +966,7 @@ __global__ __launch_bounds__(256) void mfma_pipe_kernel(MfmaArgs a) {
     int lr[NI], lpk[NI];
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-        const int slot = (i * 4 + wave) * 64 + lane;
+        const int slot = (i * NWV + wave) * 64 + lane;
         const int r = slot / PP;
         lr[i] = r;
         lpk[i] = (((slot % PP) - (r >> SH)) & (PP - 1)) * 8;
@@ -977,7 +978,7 @@ __global__ __launch_bounds__(256) void mfma_pipe_kernel(MfmaArgs a) {
         const bool live = it < T;  // uniform; past the end only zeros load
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
-            const int bi = i * 4 + wave;
+            const int bi = i * NWV + wave;
             const int k = ic * KC + lpk[i];
             const uint32_t m0 = st + (uint32_t)bi * 1024u;
             if (bi < XB) {
@@ -1288,7 +1289,7 @@ hipError_t launch_mfma_xs(const LaunchShape &sh, const proj_tactic_t &t, hipStre
     return hipErrorInvalidValue;
 }
 
-template <int MT, int NTB, int WM, int WK, int KC, int D>
+template <int MT, int NTB, int WM, int WK, int KC, int D, int NWV>
 hipError_t launch_mfma_pipe_inst(const LaunchShape &sh, const proj_tactic_t &t,
                                  hipStream_t stream) {
     const int ks = slice_len(sh.K, t);
@@ -1298,25 +1299,25 @@ hipError_t launch_mfma_pipe_inst(const LaunchShape &sh, const proj_tactic_t &t,
     static size_t lds_allowed = 64 * 1024;
     if (lds > lds_allowed) {
         hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void *>(&mfma_pipe_kernel<MT, NTB, WM, WK, KC, D>),
+            reinterpret_cast<const void *>(&mfma_pipe_kernel<MT, NTB, WM, WK, KC, D, NWV>),
             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
         if (e != hipSuccess) return e;
         lds_allowed = lds;
     }
     MfmaArgs a{sh.x, sh.ldx, sh.W, sh.y, sh.ws, fused_counters(sh, g, S), sh.N, sh.K, sh.B,
                ks, S};
-    hipLaunchKernelGGL((mfma_pipe_kernel<MT, NTB, WM, WK, KC, D>), dim3((unsigned)g, S), dim3(256),
-                       lds, stream, a);
+    hipLaunchKernelGGL((mfma_pipe_kernel<MT, NTB, WM, WK, KC, D, NWV>), dim3((unsigned)g, S),
+                       dim3(NWV * 64), lds, stream, a);
     return hipGetLastError();
 }
 
 hipError_t launch_mfma_pipe(const LaunchShape &sh, const proj_tactic_t &t, hipStream_t st) {
     // rows = N tiles per group; waves = waves along M; kw = waves along K;
-    // kc = K chunk; depth = LDS stages
-#define TP1_PIPE_CASE(BC, NTB, WM, WK, KC, D)                                         \
+    // kc = K chunk; depth = LDS stages; nw = waves per workgroup
+#define TP1_PIPE_CASE(BC, NTB, WM, WK, KC, D, NWV)                                    \
     if (t.bcap == BC && t.rows == NTB && t.waves == WM && t.kw == WK && t.kc == KC && \
-        t.depth == D)                                                                 \
-        return launch_mfma_pipe_inst<BC / 16, NTB, WM, WK, KC, D>(sh, t, st);
+        t.depth == D && t.nw == NWV)                                                  \
+        return launch_mfma_pipe_inst<BC / 16, NTB, WM, WK, KC, D, NWV>(sh, t, st);
     TP1_PIPE_INSTANCES(TP1_PIPE_CASE)
 #undef TP1_PIPE_CASE
     return hipErrorInvalidValue;
@@ -1394,8 +1395,8 @@ int kernel_name(const LaunchShape &sh, const proj_tactic_t &t, char *buf, size_t
         n = snprintf(buf, len, "mfma_xs_kernel<%d, %d, %d, %d, %d>%s", t.bcap / 16, t.rows,
                      t.waves, t.kc, t.depth, split ? "+splitk_reduce" : "");
     else if (t.kernel == PROJ_KERNEL_MFMA_PIPE)
-        n = snprintf(buf, len, "mfma_pipe_kernel<%d, %d, %d, %d, %d, %d>%s", t.bcap / 16,
-                     t.rows, t.waves, t.kw, t.kc, t.depth, split ? "+splitk_reduce" : "");
+        n = snprintf(buf, len, "mfma_pipe_kernel<%d, %d, %d, %d, %d, %d, %d>%s", t.bcap / 16,
+                     t.rows, t.waves, t.kw, t.kc, t.depth, t.nw, split ? "+splitk_reduce" : "");
     else
         n = snprintf(buf, len, "mfma_kernel<%d, %d, %d>%s", t.bcap / 16, t.rows,
                      mfma_ring(t.bcap / 16, t.rows), split ? "+splitk_reduce" : "");

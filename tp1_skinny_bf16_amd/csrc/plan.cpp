@@ -67,9 +67,9 @@ bool tactic_instance_exists(const proj_tactic_t &t) {
         return false;
     }
     if (t.kernel == PROJ_KERNEL_MFMA_PIPE) {
-#define TP1_PIPE_MATCH(BC, NTB, WM, WK, KC, D)                                           \
+#define TP1_PIPE_MATCH(BC, NTB, WM, WK, KC, D, NWV)                                      \
         if (t.bcap == BC && t.rows == NTB && t.waves == WM && t.kw == WK && t.kc == KC && \
-            t.depth == D)                                                                 \
+            t.depth == D && t.nw == NWV)                                                  \
             return true;
         TP1_PIPE_INSTANCES(TP1_PIPE_MATCH)
 #undef TP1_PIPE_MATCH
@@ -156,17 +156,17 @@ int check_tactic(int N, int K, int bin, const proj_tactic_t &t) {
     } else if (t.kc != 0 || t.depth != 0) {
         return PROJ_EINVAL;
     }
-    if (t.kernel != PROJ_KERNEL_MFMA_PIPE && t.kw != 0) return PROJ_EINVAL;
+    if (t.kernel != PROJ_KERNEL_MFMA_PIPE && (t.kw != 0 || t.nw != 0)) return PROJ_EINVAL;
     return PROJ_OK;
 }
 
 proj_tactic_t default_tactic(int N, int K, int bin, int num_cus) {
     // The rule the measured table follows on MI355X: the IEEE weight stream
-    // for 1-2 rows, the pipelined shared-tile MFMA kernel up to 32 rows (one
-    // workgroup per compute unit, K split until a workgroup holds about one
-    // 16*rows-row group), and above that the shared-tile MFMA kernel with K
-    // split so that each workgroup holds about one 128-row group (2
-    // workgroups per compute unit).
+    // for 1-2 rows, and above that the pipelined shared-tile MFMA kernel
+    // with eight waves and one workgroup per compute unit, its tile growing
+    // with the batch (16x64 with two waves along K up to 16 rows, then
+    // 32x128, 64x128, 128x256 and 256x128) and K split so that a
+    // workgroup's row range is about one weight group.
     proj_tactic_t t{};
     if (num_cus < 1) num_cus = 256;
     if (bin <= 2) {
@@ -179,33 +179,24 @@ proj_tactic_t default_tactic(int N, int K, int bin, int num_cus) {
         while (stream_lds_bytes(K, t) > 80 * 1024 && t.split < 16) ++t.split;
         return t;
     }
-    if (bin <= 32) {
-        t.kernel = PROJ_KERNEL_MFMA_PIPE;
-        t.bcap = bin <= 16 ? 16 : 32;
-        t.rows = bin <= 16 ? 4 : 8;
-        t.waves = bin <= 16 ? 1 : 2;
-        t.kc = 128;
-        t.depth = bin <= 16 ? 4 : 3;
-        t.kw = 1;
-        t.wpc = 1;
-        const long group = 16L * t.rows;
-        const long rows_per_block = std::max(1L, (long)N / num_cus);
-        int S = (int)std::min(4L, (group + rows_per_block - 1) / rows_per_block);
-        while (S > 1 && (K + S - 1) / S < 128) --S;  // keep at least one chunk per slice
-        t.split = std::max(1, S);
-        return t;
-    }
-    t.kernel = PROJ_KERNEL_MFMA_XS;
+    t.kernel = PROJ_KERNEL_MFMA_PIPE;
     t.bcap = std::max(16, next_pow2(bin));
-    t.kc = 128;
-    t.depth = 1;
-    t.wpc = t.bcap >= 256 ? 1 : 2;
-    t.rows = t.bcap >= 128 ? 4 : 8;
-    t.waves = t.bcap == 16 ? 1 : (t.bcap <= 64 ? 2 : 4);
-    const long blocks = (long)num_cus * t.wpc;
-    const long rows_per_block = std::max(1L, (long)N / blocks);
-    int S = (int)std::min(4L, std::max(1L, (16L * t.rows + rows_per_block / 2) / rows_per_block));
-    while (S > 1 && (K + S - 1) / S < 128) --S;  // keep at least one chunk per slice
+    t.nw = 8;
+    t.kw = 1;
+    t.wpc = 1;
+    t.depth = 3;
+    switch (t.bcap) {
+    case 16: t.rows = 4; t.waves = 1; t.kw = 2; t.kc = 256; break;
+    case 32: t.rows = 8; t.waves = 2; t.kc = 128; break;
+    case 64: t.rows = 8; t.waves = 2; t.kc = 128; break;
+    case 128: t.rows = 16; t.waves = 2; t.kc = 64; break;
+    default: t.rows = 8; t.waves = 4; t.kc = 64; break;
+    }
+    const long group = 16L * t.rows;
+    const long rows_per_cu = std::max(1L, (long)N / num_cus);
+    const long cap = t.bcap >= 64 ? 8 : 4;
+    int S = (int)std::min(cap, std::max(1L, (group + rows_per_cu / 2) / rows_per_cu));
+    while (S > 1 && (K + S - 1) / S < t.kc) --S;  // keep at least one chunk per slice
     t.split = S;
     return t;
 }

@@ -34,18 +34,24 @@ struct PlanCore {
     X(64, 4, 4, 128, 1) X(64, 8, 2, 128, 1) X(64, 8, 2, 256, 1) X(128, 4, 2, 128, 1) \
     X(128, 4, 4, 128, 1) X(256, 4, 4, 128, 1) X(256, 2, 4, 128, 1)
 
-// The compiled pipelined MFMA instances: X(bcap, rows, waves, kw, kc, depth).
+// The compiled pipelined MFMA instances:
+// X(bcap, rows, waves, kw, kc, depth, nw).
 #define TP1_PIPE_INSTANCES(X)                                                               \
-    X(16, 4, 1, 1, 128, 3) X(16, 4, 1, 1, 128, 4) X(16, 4, 1, 1, 128, 6)                    \
-    X(16, 4, 1, 1, 256, 3) X(16, 8, 1, 1, 128, 3) X(16, 8, 1, 1, 128, 4)                    \
-    X(16, 2, 1, 2, 256, 6) X(16, 2, 1, 2, 256, 4) X(16, 2, 1, 2, 128, 8)                    \
-    X(16, 1, 1, 4, 256, 4) X(16, 1, 1, 4, 256, 6) X(32, 4, 1, 1, 128, 4)                    \
-    X(32, 4, 1, 1, 128, 6) X(32, 4, 2, 1, 64, 8) X(32, 8, 2, 1, 128, 3)                     \
-    X(32, 2, 1, 2, 256, 4) X(32, 2, 2, 1, 256, 4) X(64, 4, 2, 1, 64, 8)                     \
-    X(64, 4, 2, 1, 128, 4) X(64, 4, 4, 1, 64, 8) X(64, 8, 2, 1, 64, 4)                      \
-    X(64, 8, 2, 1, 64, 6) X(128, 4, 4, 1, 64, 6) X(128, 4, 4, 1, 32, 12)                    \
-    X(128, 8, 4, 1, 64, 4) X(128, 8, 4, 1, 32, 8) X(256, 4, 4, 1, 32, 7)                    \
-    X(256, 4, 4, 1, 64, 3) X(256, 8, 4, 1, 32, 6) X(256, 8, 4, 1, 64, 3)
+    X(16, 4, 1, 1, 128, 3, 4) X(16, 4, 1, 1, 128, 4, 4) X(16, 4, 1, 1, 128, 6, 4)           \
+    X(16, 4, 1, 1, 256, 3, 4) X(16, 8, 1, 1, 128, 3, 4) X(16, 8, 1, 1, 128, 4, 4)           \
+    X(16, 2, 1, 2, 256, 6, 4) X(16, 2, 1, 2, 256, 4, 4) X(16, 2, 1, 2, 128, 8, 4)           \
+    X(16, 1, 1, 4, 256, 4, 4) X(16, 1, 1, 4, 256, 6, 4) X(32, 4, 1, 1, 128, 4, 4)           \
+    X(32, 4, 1, 1, 128, 6, 4) X(32, 4, 2, 1, 64, 8, 4) X(32, 8, 2, 1, 128, 3, 4)            \
+    X(32, 2, 1, 2, 256, 4, 4) X(32, 2, 2, 1, 256, 4, 4) X(64, 4, 2, 1, 64, 8, 4)            \
+    X(64, 4, 2, 1, 128, 4, 4) X(64, 4, 4, 1, 64, 8, 4) X(64, 8, 2, 1, 64, 4, 4)             \
+    X(64, 8, 2, 1, 64, 6, 4) X(128, 4, 4, 1, 64, 6, 4) X(128, 4, 4, 1, 32, 12, 4)           \
+    X(128, 8, 4, 1, 64, 4, 4) X(128, 8, 4, 1, 32, 8, 4) X(256, 4, 4, 1, 32, 7, 4)           \
+    X(256, 4, 4, 1, 64, 3, 4) X(256, 8, 4, 1, 32, 6, 4) X(256, 8, 4, 1, 64, 3, 4)           \
+    X(64, 16, 2, 1, 64, 3, 8) X(64, 8, 2, 1, 128, 3, 8) X(64, 16, 1, 1, 64, 3, 8)           \
+    X(128, 16, 2, 1, 64, 3, 8) X(128, 8, 2, 1, 64, 4, 8) X(128, 16, 4, 1, 32, 4, 8)         \
+    X(256, 16, 4, 1, 32, 4, 8) X(256, 8, 4, 1, 64, 3, 8)          \
+    X(16, 8, 1, 1, 256, 2, 8) X(16, 4, 1, 2, 256, 3, 8) X(32, 8, 2, 1, 128, 3, 8)           \
+    X(64, 8, 4, 1, 128, 3, 8) X(256, 8, 8, 1, 64, 3, 8)
 
 // LDS bytes of an MFMA_XS tactic (x and W chunk tiles, 16 bytes of row pad).
 size_t mfma_xs_lds_bytes(const proj_tactic_t &t);

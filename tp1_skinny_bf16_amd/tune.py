@@ -66,17 +66,28 @@ def candidates(bin_: int, full: bool = False):
           128: ((4, 2, 128, 1), (4, 4, 128, 1)), 256: ((4, 4, 128, 1), (2, 4, 128, 1))}[bc]
     for (rows, waves, kc, depth), split, wpc in itertools.product(xs, (1, 2, 3, 4), (1, 2)):
         out.append(Tactic(KERNEL_MFMA_XS, bc, split, rows, waves, wpc, kc, depth))
-    pipe = {16: ((4, 1, 1, 128, 3), (4, 1, 1, 128, 4), (4, 1, 1, 128, 6), (4, 1, 1, 256, 3),
-                 (8, 1, 1, 128, 3), (8, 1, 1, 128, 4), (2, 1, 2, 256, 6), (2, 1, 2, 256, 4),
-                 (2, 1, 2, 128, 8), (1, 1, 4, 256, 4), (1, 1, 4, 256, 6)),
-            32: ((4, 1, 1, 128, 4), (4, 1, 1, 128, 6), (4, 2, 1, 64, 8), (8, 2, 1, 128, 3),
-                 (2, 1, 2, 256, 4), (2, 2, 1, 256, 4)),
-            64: ((4, 2, 1, 64, 8), (4, 2, 1, 128, 4), (4, 4, 1, 64, 8), (8, 2, 1, 64, 4),
-                 (8, 2, 1, 64, 6)),
-            128: ((4, 4, 1, 64, 6), (4, 4, 1, 32, 12), (8, 4, 1, 64, 4), (8, 4, 1, 32, 8)),
-            256: ((4, 4, 1, 32, 7), (4, 4, 1, 64, 3), (8, 4, 1, 32, 6), (8, 4, 1, 64, 3))}[bc]
-    for (rows, waves, kw, kc, depth), split, wpc in itertools.product(pipe, (1, 2, 3, 4), (1, 2)):
-        out.append(Tactic(KERNEL_MFMA_PIPE, bc, split, rows, waves, wpc, kc, depth, kw))
+    pipe = {16: ((4, 1, 1, 128, 3, 4), (4, 1, 1, 128, 4, 4), (4, 1, 1, 128, 6, 4),
+                 (4, 1, 1, 256, 3, 4), (8, 1, 1, 128, 3, 4), (8, 1, 1, 128, 4, 4),
+                 (2, 1, 2, 256, 6, 4), (2, 1, 2, 256, 4, 4), (2, 1, 2, 128, 8, 4),
+                 (1, 1, 4, 256, 4, 4), (1, 1, 4, 256, 6, 4), (8, 1, 1, 256, 2, 8),
+                 (4, 1, 2, 256, 3, 8)),
+            32: ((4, 1, 1, 128, 4, 4), (4, 1, 1, 128, 6, 4), (4, 2, 1, 64, 8, 4),
+                 (8, 2, 1, 128, 3, 4), (2, 1, 2, 256, 4, 4), (2, 2, 1, 256, 4, 4),
+                 (8, 2, 1, 128, 3, 8)),
+            64: ((4, 2, 1, 64, 8, 4), (4, 2, 1, 128, 4, 4), (4, 4, 1, 64, 8, 4),
+                 (8, 2, 1, 64, 4, 4), (8, 2, 1, 64, 6, 4), (16, 2, 1, 64, 3, 8),
+                 (8, 2, 1, 128, 3, 8), (16, 1, 1, 64, 3, 8), (8, 4, 1, 128, 3, 8)),
+            128: ((4, 4, 1, 64, 6, 4), (4, 4, 1, 32, 12, 4), (8, 4, 1, 64, 4, 4),
+                  (8, 4, 1, 32, 8, 4), (16, 2, 1, 64, 3, 8), (8, 2, 1, 64, 4, 8),
+                  (16, 4, 1, 32, 4, 8)),
+            256: ((4, 4, 1, 32, 7, 4), (4, 4, 1, 64, 3, 4), (8, 4, 1, 32, 6, 4),
+                  (8, 4, 1, 64, 3, 4), (16, 4, 1, 32, 4, 8),
+                  (8, 4, 1, 64, 3, 8), (8, 8, 1, 64, 3, 8))}[bc]
+    for (rows, waves, kw, kc, depth, nw), split, wpc in itertools.product(
+            pipe, (1, 2, 3, 4, 6, 8), (1, 2)):
+        if (split > 4 and bc < 64) or (nw == 8 and wpc > 1):
+            continue
+        out.append(Tactic(KERNEL_MFMA_PIPE, bc, split, rows, waves, wpc, kc, depth, kw, nw))
     return out
 
 
@@ -154,25 +165,31 @@ def table_rows(result) -> str:
         t = dict(r["chosen"]["tactic"])
         if t["kernel"] == "mfma_pipe" and not t.get("kw"):
             t["kw"] = 1  # measured before the field existed: one wave along K
+        if t["kernel"] == "mfma_pipe" and not t.get("nw"):
+            t["nw"] = 4  # measured before the field existed: four waves
         k = {"stream": "PROJ_KERNEL_STREAM", "mfma": "PROJ_KERNEL_MFMA",
              "stream_dot2": "PROJ_KERNEL_STREAM_DOT2",
              "mfma_lds": "PROJ_KERNEL_MFMA_LDS", "mfma_xs": "PROJ_KERNEL_MFMA_XS",
              "mfma_pipe": "PROJ_KERNEL_MFMA_PIPE"}[t["kernel"]]
         lines.append(f"    {{{result['N']}, {result['K']}, {b}, {{{k}, {t['bcap']}, {t['split']}, "
                      f"{t['rows']}, {t['waves']}, {t['wpc']}, {t.get('kc', 0)}, "
-                     f"{t.get('depth', 0)}, {t.get('kw', 0)}}}}},  // "
+                     f"{t.get('depth', 0)}, {t.get('kw', 0)}, {t.get('nw', 0)}}}}},  // "
                      f"{r['chosen']['us']} us, {r['GBps']} GB/s")
     return "\n".join(lines)
 
 
 def emit_table(paths) -> str:
-    """C++ rows of tactics_table.cpp from tuner JSON files (later files win)."""
+    """C++ rows of tactics_table.cpp from tuner JSON files: per (N, K, bin)
+    the fastest chosen tactic over the runs given (runs on different boxes
+    differ by a few percent, so no single run is the reference)."""
     chosen = {}
     for path in paths:
         with open(path) as f:
             for res in json.load(f):
                 for b, r in res["bins"].items():
-                    chosen[(res["N"], res["K"], int(b))] = r
+                    key = (res["N"], res["K"], int(b))
+                    if key not in chosen or r["chosen"]["us"] < chosen[key]["chosen"]["us"]:
+                        chosen[key] = r
     merged = {}
     for (N, K, b), r in chosen.items():
         merged.setdefault((N, K), {"N": N, "K": K, "bins": {}})["bins"][b] = r
@@ -186,18 +203,22 @@ def emit_table(paths) -> str:
 
 def summarize(paths) -> str:
     """Markdown of the measured tables: chosen tactic per bin, the best stream
-    and best MFMA candidate, and the crossover (later files win)."""
+    and best MFMA candidate, and the crossover (per bin the fastest run, as
+    emit_table picks it)."""
     chosen = {}
     for path in paths:
         with open(path) as f:
             for res in json.load(f):
                 for b, r in res["bins"].items():
-                    chosen[(res["N"], res["K"], int(b))] = r
+                    key = (res["N"], res["K"], int(b))
+                    if key not in chosen or r["chosen"]["us"] < chosen[key]["chosen"]["us"]:
+                        chosen[key] = r
     lines = []
     for (N, K) in sorted({(n, k) for n, k, _ in chosen}):
         bins = sorted(b for n, k, b in chosen if (n, k) == (N, K))
         lines += [f"## {N} x {K}", "",
-                  "| bin | chosen kernel | tactic (bcap, split, rows, waves, wpc, kc, depth, kw) | us "
+                  "| bin | chosen kernel | tactic (bcap, split, rows, waves, wpc, kc, depth, kw, nw) "
+                  "| us "
                   "| GB/s "
                   "| best stream us | best MFMA us | candidates |",
                   "|---|---|---|---|---|---|---|---|"]
@@ -209,7 +230,7 @@ def summarize(paths) -> str:
                 cross = b
             lines.append(f"| {b} | `{r['chosen']['kernel']}` | {t['bcap']}, {t['split']}, {t['rows']}, "
                          f"{t['waves']}, {t['wpc']}, {t.get('kc', 0)}, {t.get('depth', 0)}, "
-                         f"{t.get('kw', 0)} | "
+                         f"{t.get('kw', 0)}, {t.get('nw', 0)} | "
                          f"{r['chosen']['us']} | {r['GBps']} | "
                          f"{r.get('best_stream_us')} | {r.get('best_mfma_us')} | {r['n_candidates']} |")
         lines += ["", f"Crossover (first bin whose best tactic is an MFMA kernel): {cross}", ""]

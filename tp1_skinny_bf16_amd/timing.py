@@ -9,6 +9,7 @@ layers does.
 from __future__ import annotations
 
 import statistics
+import time
 
 import torch
 
@@ -31,27 +32,38 @@ def rotation_copies(W0: torch.Tensor, min_total_bytes: float = 1.0e9,
     return copies
 
 
-def time_calls(calls, warmup: int = 5, reps: int = 50):
+def time_calls(calls, warmup: int = 5, reps: int = 50, warm_seconds: float = 0.25):
     """Time a list of zero-argument callables, run round-robin.
 
     Returns per-call durations in microseconds (GPU event time of each call,
-    enqueued back to back on the current stream) plus the mean over the whole
-    back-to-back run (total / number of calls).
+    each bracketed by its own pair of events) and, from a second pass of the
+    same calls enqueued back to back between one pair of events, the mean
+    time per call without per-call markers.
     """
     stream = torch.cuda.current_stream()
     n = len(calls)
     for i in range(warmup * n):
         calls[i % n]()
+    # keep the GPU busy for a moment first: after host-side work the clocks
+    # have dropped, and the first timings would run slow
+    t_end = time.perf_counter() + warm_seconds
+    while time.perf_counter() < t_end:
+        for c in calls:
+            c()
+        torch.cuda.synchronize()
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(reps)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    t0.record(stream)
     for i in range(reps):
         starts[i].record(stream)
         calls[i % n]()
         ends[i].record(stream)
+    torch.cuda.synchronize()
+    t0.record(stream)
+    for i in range(reps):
+        calls[i % n]()
     t1.record(stream)
     torch.cuda.synchronize()
     per = [s.elapsed_time(e) * 1e3 for s, e in zip(starts, ends)]

@@ -128,7 +128,7 @@ def measure(N: int, K: int, bins, reps: int = 40, log=None, full: bool = False,
                 continue
             calls = [(lambda W=W: plan.run_ptr(b, xb.data_ptr(), K, W.data_ptr(),
                                                y.data_ptr(), st)) for W in copies]
-            r = time_calls(calls, warmup=2, reps=reps)
+            r = time_calls(calls, warmup=2, reps=reps, warm_seconds=0.0)
             rows.append({"tactic": t.as_dict(), "us": round(r["us_median"], 2),
                          "kernel": plan.kernel_name(b)})
         rows.sort(key=_key)

@@ -118,10 +118,11 @@ def candidate_tactics(N: int, K: int, bin_: int):
                  (4, 1, 1, 256, 3, 4), (8, 1, 1, 128, 3, 4), (8, 1, 1, 128, 4, 4),
                  (2, 1, 2, 256, 6, 4), (2, 1, 2, 256, 4, 4), (2, 1, 2, 128, 8, 4),
                  (1, 1, 4, 256, 4, 4), (1, 1, 4, 256, 6, 4), (8, 1, 1, 256, 2, 8),
-                 (4, 1, 2, 256, 3, 8)),
+                 (4, 1, 2, 256, 3, 8), (2, 1, 4, 256, 6, 8),
+                 (2, 1, 4, 256, 4, 8), (1, 1, 8, 256, 4, 8)),
             32: ((4, 1, 1, 128, 4, 4), (4, 1, 1, 128, 6, 4), (4, 2, 1, 64, 8, 4),
                  (8, 2, 1, 128, 3, 4), (2, 1, 2, 256, 4, 4), (2, 2, 1, 256, 4, 4),
-                 (8, 2, 1, 128, 3, 8)),
+                 (8, 2, 1, 128, 3, 8), (2, 1, 4, 256, 4, 8)),
             64: ((4, 2, 1, 64, 8, 4), (4, 2, 1, 128, 4, 4), (4, 4, 1, 64, 8, 4),
                  (8, 2, 1, 64, 4, 4), (8, 2, 1, 64, 6, 4), (16, 2, 1, 64, 3, 8),
                  (8, 2, 1, 128, 3, 8), (16, 1, 1, 64, 3, 8), (8, 4, 1, 128, 3, 8)),

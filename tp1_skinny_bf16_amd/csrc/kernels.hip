@@ -95,20 +95,42 @@ __device__ __forceinline__ float wave_sum(float v) {
     return ((a + b) + c) + d;
 }
 
+// s_waitcnt vmcnt(N) leaving the other counters alone (gfx9 encoding).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N <= 63, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// A split-K partial.  With the in-kernel reduction (through = true) it is an
+// agent-scope store, which writes through the XCD's L2 to the device-coherent
+// level, so the workgroup that sums it (possibly on another XCD) reads it
+// without any L2 write-back; with the two-pass reduction a plain store does,
+// since the kernel boundary orders it before splitk_reduce.
+__device__ __forceinline__ void store_partial(float *p, float v, bool through) {
+    if (through)
+        __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else
+        *p = v;
+}
+
 // ---------------------------------------------------------------------------
 // Fused split-K reduction.  When K is split over S workgroups (gridDim.y),
 // each workgroup writes its FP32 partials for rows [row0, row0 + rows) to
-// the workspace, makes them visible device-wide, and counts its arrival on
-// an integer counter of its row range.  The workgroup that arrives last sums
-// the S partials in the fixed order s = 0..S-1 (the same order as the
-// two-pass splitk_reduce, so the result does not depend on arrival order),
-// rounds once to BF16, and resets the counter for the next call.  Called by
-// every thread of the workgroup, after its last partial store.
+// the workspace through store_partial, waits until those stores have
+// completed, and counts its arrival on an integer counter of its row range.
+// The workgroup that arrives last reads the S partials with agent-scope
+// loads (from the device-coherent level, not a stale L2 line) and sums them
+// in the fixed order s = 0..S-1 (the order of the two-pass splitk_reduce, so
+// the result does not depend on arrival order), rounds once to BF16, and
+// resets the counter for the next call.  Called by every thread of the
+// workgroup, after its last partial store.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void splitk_fixup(const float *ws, uint16_t *y, int *cnt, int N,
                                              int B, int row0, int rows) {
     __shared__ int last;
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // partials before the arrival
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);  // keep the partial stores above the wait
+    wait_vmcnt<0>();                          // this thread's partials have completed
     __syncthreads();
     if (threadIdx.x == 0) {
         const int old = __hip_atomic_fetch_add(cnt + blockIdx.x, 1, __ATOMIC_RELAXED,
@@ -117,17 +139,19 @@ __device__ __forceinline__ void splitk_fixup(const float *ws, uint16_t *y, int *
     }
     __syncthreads();
     if (!last) return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // the other slices' partials
     const int S = gridDim.y;
     const size_t slice = (size_t)B * N;
     for (int i = threadIdx.x; i < rows * B; i += blockDim.x) {
         const int b = i / rows, r = i - (i / rows) * rows;
         const size_t o = (size_t)b * N + row0 + r;
-        float acc = ws[o];
-        for (int k = 1; k < S; ++k) acc += ws[k * slice + o];
+        float acc = __hip_atomic_load(ws + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        for (int k = 1; k < S; ++k)
+            acc += __hip_atomic_load(ws + k * slice + o, __ATOMIC_RELAXED,
+                                     __HIP_MEMORY_SCOPE_AGENT);
         y[o] = to_bf16(acc);
     }
-    if (threadIdx.x == 0) cnt[blockIdx.x] = 0;
+    if (threadIdx.x == 0)
+        __hip_atomic_store(cnt + blockIdx.x, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------------------
@@ -227,7 +251,7 @@ __global__ __launch_bounds__(512) void stream_kernel(StreamArgs a) {
         if (a.S == 1)
             a.y[(size_t)b * a.N + row] = to_bf16(v);
         else
-            a.ws[((size_t)s * a.B + b) * a.N + row] = v;
+            store_partial(a.ws + ((size_t)s * a.B + b) * a.N + row, v, a.cnt != nullptr);
     };
 
     if (T > 0) {
@@ -409,7 +433,7 @@ __global__ __launch_bounds__(256) void mfma_kernel(MfmaArgs a) {
         if (a.S == 1)
             a.y[(size_t)row * a.N + col] = to_bf16(v);
         else
-            a.ws[((size_t)s * a.B + row) * a.N + col] = v;
+            store_partial(a.ws + ((size_t)s * a.B + row) * a.N + col, v, a.cnt != nullptr);
     };
 
     if (T > 0) {
@@ -580,7 +604,7 @@ __global__ __launch_bounds__(256) void mfma_lds_kernel(MfmaArgs a) {
         if (a.S == 1)
             a.y[(size_t)row * a.N + col] = to_bf16(v);
         else
-            a.ws[((size_t)s * a.B + row) * a.N + col] = v;
+            store_partial(a.ws + ((size_t)s * a.B + row) * a.N + col, v, a.cnt != nullptr);
     };
 
     if (T > 0) {
@@ -762,7 +786,7 @@ __global__ __launch_bounds__(256) void mfma_xs_kernel(MfmaArgs a) {
         if (a.S == 1)
             a.y[(size_t)row * a.N + col] = to_bf16(v);
         else
-            a.ws[((size_t)s * a.B + row) * a.N + col] = v;
+            store_partial(a.ws + ((size_t)s * a.B + row) * a.N + col, v, a.cnt != nullptr);
     };
 
     // PD register sets: chunks t+1 .. t+PD are in flight while chunk t is
@@ -911,13 +935,6 @@ __device__ __forceinline__ void lds_load16_cached(const void *src, uint32_t m0) 
 }
 #pragma clang diagnostic pop
 
-// s_waitcnt vmcnt(N) leaving the other counters alone (gfx9 encoding).
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N <= 63, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
 template <int MT, int NTB, int WM, int WK, int KC, int D, int NWV>
 __global__ __launch_bounds__(NWV * 64) void mfma_pipe_kernel(MfmaArgs a) {
     static_assert(NWV == 4 || NWV == 8, "four or eight waves");
@@ -1003,7 +1020,7 @@ __global__ __launch_bounds__(NWV * 64) void mfma_pipe_kernel(MfmaArgs a) {
         if (a.S == 1)
             a.y[(size_t)row * a.N + col] = to_bf16(v);
         else
-            a.ws[((size_t)s * a.B + row) * a.N + col] = v;
+            store_partial(a.ws + ((size_t)s * a.B + row) * a.N + col, v, a.cnt != nullptr);
     };
 
     f32x4 acc[MTW][NTW];

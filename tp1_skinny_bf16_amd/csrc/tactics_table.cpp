@@ -19,33 +19,33 @@ struct Entry {
 // calls per candidate; each comment gives the chosen tactic's time and
 // achieved bandwidth (weight + x + y bytes).
 const Entry kTable[] = {
-    {7168, 12288, 1, {PROJ_KERNEL_STREAM_DOT2, 1, 1, 4, 4, 8, 0, 0, 0, 0}},  // 32.34 us, 5448.4 GB/s
+    {7168, 12288, 1, {PROJ_KERNEL_STREAM_DOT2, 1, 1, 4, 4, 8, 0, 0, 0, 0}},  // 32.18 us, 5475.4 GB/s
     {7168, 12288, 2, {PROJ_KERNEL_MFMA_PIPE, 16, 4, 4, 1, 1, 256, 3, 2, 8}},  // 32.58 us, 5409.4 GB/s
     {7168, 12288, 4, {PROJ_KERNEL_MFMA_PIPE, 16, 4, 4, 1, 1, 256, 3, 2, 8}},  // 32.68 us, 5395.2 GB/s
     {7168, 12288, 8, {PROJ_KERNEL_MFMA_PIPE, 16, 4, 4, 1, 1, 256, 3, 2, 8}},  // 32.76 us, 5386.8 GB/s
-    {7168, 12288, 16, {PROJ_KERNEL_MFMA_PIPE, 16, 4, 4, 1, 1, 256, 3, 2, 8}},  // 33.31 us, 5307.2 GB/s
+    {7168, 12288, 16, {PROJ_KERNEL_MFMA_PIPE, 16, 4, 4, 1, 1, 256, 3, 2, 8}},  // 33.2 us, 5324.8 GB/s
     {7168, 12288, 32, {PROJ_KERNEL_MFMA_PIPE, 32, 4, 8, 2, 1, 128, 3, 1, 8}},  // 34.44 us, 5151.2 GB/s
     {7168, 12288, 64, {PROJ_KERNEL_MFMA_PIPE, 64, 4, 8, 2, 1, 128, 3, 1, 8}},  // 38.64 us, 4623.5 GB/s
     {7168, 12288, 128, {PROJ_KERNEL_MFMA_PIPE, 128, 8, 16, 2, 1, 64, 3, 1, 8}},  // 48.03 us, 3771.4 GB/s
-    {7168, 12288, 256, {PROJ_KERNEL_MFMA_PIPE, 256, 4, 8, 4, 1, 64, 3, 1, 8}},  // 73.15 us, 2544.4 GB/s
-    {14560, 7168, 1, {PROJ_KERNEL_MFMA_PIPE, 16, 1, 4, 1, 1, 256, 3, 2, 8}},  // 34.95 us, 5973.6 GB/s
+    {7168, 12288, 256, {PROJ_KERNEL_MFMA_PIPE, 256, 4, 8, 4, 1, 64, 3, 1, 8}},  // 72.45 us, 2569.0 GB/s
+    {14560, 7168, 1, {PROJ_KERNEL_MFMA_PIPE, 16, 1, 4, 1, 1, 256, 3, 2, 8}},  // 34.52 us, 6048.0 GB/s
     {14560, 7168, 2, {PROJ_KERNEL_MFMA_PIPE, 16, 1, 4, 1, 1, 256, 3, 2, 8}},  // 34.95 us, 5974.8 GB/s
-    {14560, 7168, 4, {PROJ_KERNEL_MFMA_PIPE, 16, 1, 4, 1, 1, 256, 3, 2, 8}},  // 35.0 us, 5968.7 GB/s
+    {14560, 7168, 4, {PROJ_KERNEL_MFMA_PIPE, 16, 1, 4, 1, 1, 256, 3, 2, 8}},  // 34.8 us, 6003.0 GB/s
     {14560, 7168, 8, {PROJ_KERNEL_MFMA_PIPE, 16, 1, 4, 1, 1, 256, 3, 2, 8}},  // 34.79 us, 6009.8 GB/s
-    {14560, 7168, 16, {PROJ_KERNEL_MFMA_PIPE, 16, 1, 4, 1, 1, 256, 3, 2, 8}},  // 34.93 us, 5995.6 GB/s
-    {14560, 7168, 32, {PROJ_KERNEL_MFMA_PIPE, 32, 2, 8, 2, 1, 128, 3, 1, 8}},  // 38.22 us, 5497.7 GB/s
+    {14560, 7168, 16, {PROJ_KERNEL_MFMA_PIPE, 16, 1, 4, 1, 1, 256, 3, 2, 8}},  // 34.38 us, 6091.5 GB/s
+    {14560, 7168, 32, {PROJ_KERNEL_MFMA_PIPE, 32, 2, 8, 2, 1, 128, 3, 1, 8}},  // 38.09 us, 5516.5 GB/s
     {14560, 7168, 64, {PROJ_KERNEL_MFMA_PIPE, 64, 2, 8, 2, 1, 128, 3, 1, 8}},  // 42.77 us, 4945.4 GB/s
-    {14560, 7168, 128, {PROJ_KERNEL_MFMA_PIPE, 128, 4, 16, 2, 1, 64, 3, 1, 8}},  // 54.97 us, 3898.4 GB/s
-    {14560, 7168, 256, {PROJ_KERNEL_MFMA_PIPE, 256, 2, 8, 4, 1, 64, 3, 1, 8}},  // 86.25 us, 2549.1 GB/s
+    {14560, 7168, 128, {PROJ_KERNEL_MFMA_PIPE, 128, 4, 16, 2, 1, 64, 3, 1, 8}},  // 53.79 us, 3983.9 GB/s
+    {14560, 7168, 256, {PROJ_KERNEL_MFMA_PIPE, 256, 2, 8, 4, 1, 64, 3, 1, 8}},  // 84.99 us, 2586.9 GB/s
     {49376, 7168, 1, {PROJ_KERNEL_MFMA_XS, 16, 1, 8, 1, 2, 128, 1, 0, 0}},  // 103.55 us, 6837.0 GB/s
-    {49376, 7168, 2, {PROJ_KERNEL_MFMA_XS, 16, 1, 8, 1, 2, 128, 1, 0, 0}},  // 104.47 us, 6777.8 GB/s
-    {49376, 7168, 4, {PROJ_KERNEL_MFMA_XS, 16, 1, 8, 1, 2, 128, 1, 0, 0}},  // 104.19 us, 6798.2 GB/s
-    {49376, 7168, 8, {PROJ_KERNEL_MFMA_XS, 16, 1, 8, 1, 2, 128, 1, 0, 0}},  // 103.57 us, 6843.3 GB/s
-    {49376, 7168, 16, {PROJ_KERNEL_MFMA_XS, 16, 1, 8, 1, 2, 128, 1, 0, 0}},  // 105.47 us, 6728.6 GB/s
-    {49376, 7168, 32, {PROJ_KERNEL_MFMA_XS, 32, 1, 8, 2, 2, 128, 1, 0, 0}},  // 108.7 us, 6545.3 GB/s
+    {49376, 7168, 2, {PROJ_KERNEL_MFMA_XS, 16, 1, 8, 1, 2, 128, 1, 0, 0}},  // 103.77 us, 6823.6 GB/s
+    {49376, 7168, 4, {PROJ_KERNEL_MFMA_XS, 16, 1, 8, 1, 2, 128, 1, 0, 0}},  // 103.95 us, 6813.9 GB/s
+    {49376, 7168, 8, {PROJ_KERNEL_MFMA_XS, 16, 1, 8, 1, 2, 128, 1, 0, 0}},  // 103.47 us, 6849.9 GB/s
+    {49376, 7168, 16, {PROJ_KERNEL_MFMA_XS, 16, 1, 8, 1, 2, 128, 1, 0, 0}},  // 104.17 us, 6812.6 GB/s
+    {49376, 7168, 32, {PROJ_KERNEL_MFMA_XS, 32, 1, 8, 2, 2, 128, 1, 0, 0}},  // 107.65 us, 6609.1 GB/s
     {49376, 7168, 64, {PROJ_KERNEL_MFMA_PIPE, 64, 1, 16, 2, 1, 64, 3, 1, 8}},  // 113.3 us, 6311.5 GB/s
     {49376, 7168, 128, {PROJ_KERNEL_MFMA_PIPE, 128, 1, 16, 2, 1, 64, 3, 1, 8}},  // 157.48 us, 4586.8 GB/s
-    {49376, 7168, 256, {PROJ_KERNEL_MFMA_PIPE, 256, 1, 8, 4, 1, 64, 3, 1, 8}},  // 275.51 us, 2674.3 GB/s
+    {49376, 7168, 256, {PROJ_KERNEL_MFMA_PIPE, 256, 1, 8, 4, 1, 64, 3, 1, 8}},  // 272.53 us, 2703.6 GB/s
 };
 }  // namespace
 

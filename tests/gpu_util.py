@@ -125,13 +125,14 @@ def candidate_tactics(N: int, K: int, bin_: int):
                  (8, 2, 1, 128, 3, 8), (2, 1, 4, 256, 4, 8)),
             64: ((4, 2, 1, 64, 8, 4), (4, 2, 1, 128, 4, 4), (4, 4, 1, 64, 8, 4),
                  (8, 2, 1, 64, 4, 4), (8, 2, 1, 64, 6, 4), (16, 2, 1, 64, 3, 8),
-                 (8, 2, 1, 128, 3, 8), (16, 1, 1, 64, 3, 8), (8, 4, 1, 128, 3, 8)),
+                 (8, 2, 1, 128, 3, 8), (16, 1, 1, 64, 3, 8), (8, 4, 1, 128, 3, 8),
+                 (8, 2, 1, 64, 6, 8)),
             128: ((4, 4, 1, 64, 6, 4), (4, 4, 1, 32, 12, 4), (8, 4, 1, 64, 4, 4),
                   (8, 4, 1, 32, 8, 4), (16, 2, 1, 64, 3, 8), (8, 2, 1, 64, 4, 8),
-                  (16, 4, 1, 32, 4, 8)),
+                  (16, 4, 1, 32, 4, 8), (8, 2, 1, 32, 8, 8), (16, 2, 1, 32, 6, 8)),
             256: ((4, 4, 1, 32, 7, 4), (4, 4, 1, 64, 3, 4), (8, 4, 1, 32, 6, 4),
                   (8, 4, 1, 64, 3, 4), (16, 4, 1, 32, 4, 8),
-                  (8, 4, 1, 64, 3, 8), (8, 8, 1, 64, 3, 8))}
+                  (8, 4, 1, 64, 3, 8), (8, 8, 1, 64, 3, 8), (8, 4, 1, 32, 6, 8))}
     for bc, shapes in pipe.items():
         if bc < bin_:
             continue

@@ -80,13 +80,14 @@ def candidates(bin_: int, full: bool = False):
                  (8, 2, 1, 128, 3, 8), (2, 1, 4, 256, 4, 8)),
             64: ((4, 2, 1, 64, 8, 4), (4, 2, 1, 128, 4, 4), (4, 4, 1, 64, 8, 4),
                  (8, 2, 1, 64, 4, 4), (8, 2, 1, 64, 6, 4), (16, 2, 1, 64, 3, 8),
-                 (8, 2, 1, 128, 3, 8), (16, 1, 1, 64, 3, 8), (8, 4, 1, 128, 3, 8)),
+                 (8, 2, 1, 128, 3, 8), (16, 1, 1, 64, 3, 8), (8, 4, 1, 128, 3, 8),
+                 (8, 2, 1, 64, 6, 8)),
             128: ((4, 4, 1, 64, 6, 4), (4, 4, 1, 32, 12, 4), (8, 4, 1, 64, 4, 4),
                   (8, 4, 1, 32, 8, 4), (16, 2, 1, 64, 3, 8), (8, 2, 1, 64, 4, 8),
-                  (16, 4, 1, 32, 4, 8)),
+                  (16, 4, 1, 32, 4, 8), (8, 2, 1, 32, 8, 8), (16, 2, 1, 32, 6, 8)),
             256: ((4, 4, 1, 32, 7, 4), (4, 4, 1, 64, 3, 4), (8, 4, 1, 32, 6, 4),
                   (8, 4, 1, 64, 3, 4), (16, 4, 1, 32, 4, 8),
-                  (8, 4, 1, 64, 3, 8), (8, 8, 1, 64, 3, 8))}[bc]
+                  (8, 4, 1, 64, 3, 8), (8, 8, 1, 64, 3, 8), (8, 4, 1, 32, 6, 8))}[bc]
     for (rows, waves, kw, kc, depth, nw), split, wpc in itertools.product(
             pipe, (1, 2, 3, 4, 6, 8), (1, 2)):
         if (split > 4 and bc < 64) or (nw == 8 and wpc > 1):

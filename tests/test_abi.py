@@ -179,3 +179,29 @@ def test_product_package_never_touches_the_oracle():
             if f.endswith((".py", ".hip", ".cpp", ".hpp", ".h")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert not re.search(r"\boracle\b", text), f"{f} mentions the oracle"
+
+
+def test_unlisted_bins_take_the_next_measured_tactic():
+    # verify-step batches (requests x (1 + speculative tokens)) are not powers
+    # of two; each takes the measured tactic of the next measured bin above it
+    p = tp.Plan(14560, 7168, [3, 6, 12, 24, 48, 96, 192], host_only=True)
+    q = tp.Plan(14560, 7168, [4, 8, 16, 32, 64, 128, 256], host_only=True)
+    for b, ref in zip([3, 6, 12, 24, 48, 96, 192], [4, 8, 16, 32, 64, 128, 256]):
+        assert p.tactic(b)[0] == q.tactic(ref)[0]
+    # above the largest measured bin there is nothing to borrow: default rule
+    r = tp.Plan(14560, 7168, [1], host_only=True)
+    assert r.tactic(1)[0].kernel in tp.KERNEL_NAMES
+
+
+def test_pipe_only_fields_are_validated():
+    p = tp.Plan(14560, 7168, [16], host_only=True)
+    ok = tp.Tactic(tp.KERNEL_MFMA_PIPE, 16, 1, 4, 1, 1, 256, 3, 2, 8)
+    p.set_tactic(16, ok)
+    for bad in [tp.Tactic(tp.KERNEL_MFMA_PIPE, 16, 1, 4, 1, 1, 256, 3, 0, 8),    # kw 0
+                tp.Tactic(tp.KERNEL_MFMA_PIPE, 16, 1, 4, 1, 1, 256, 3, 2, 4),    # not compiled
+                tp.Tactic(tp.KERNEL_MFMA_PIPE, 16, 1, 4, 1, 3, 256, 3, 2, 8),    # wpc 3
+                tp.Tactic(tp.KERNEL_MFMA_XS, 16, 1, 8, 1, 2, 128, 1, 1, 0),      # kw on XS
+                tp.Tactic(tp.KERNEL_MFMA_XS, 16, 1, 8, 1, 2, 128, 1, 0, 4),      # nw on XS
+                tp.Tactic(tp.KERNEL_STREAM, 1, 1, 4, 4, 8, 0, 0, 0, 8)]:         # nw on STREAM
+        with pytest.raises(tp.ProjError):
+            p.set_tactic(16, bad)

@@ -84,6 +84,25 @@ def test_full_config_random(name, B):
     check_random(f"{name} B={B}", y, t["x"][:B], t["W"], cols=cols)
 
 
+VERIFY_BINS = [3, 6, 12, 24, 48, 96, 192]   # requests x (1 + speculative tokens)
+
+
+@pytest.mark.parametrize("N,K", [(wl.DSA_N, wl.DSA_K), (wl.OPROJ_N, wl.OPROJ_K)])
+def test_verify_step_batches_full_shape(N, K):
+    """Plans listing verify-step batches (not powers of two) borrow the next
+    measured bin's tactic; every bin, and a batch below its bin, is exact on
+    exact-sum inputs."""
+    x, W = wl.exact_sum_case(192, N, K, seed=13)
+    Wd = W.to(DEV)
+    plan = tp.Plan(N, K, VERIFY_BINS)
+    for b in VERIFY_BINS:
+        for B in sorted({b, b - 1}):
+            y = gpu_run(plan, x[:B], Wd)
+            cols = sample_rows(N, B, K, budget=1.0e9, seed=B)
+            check_exact(f"verify N={N} K={K} B={B} {tactic_label(plan, B)}", y, x[:B], W,
+                        cols=cols)
+
+
 @pytest.mark.parametrize("N,K", [(wl.DSA_N, wl.DSA_K), (wl.OPROJ_N, wl.OPROJ_K),
                                  (wl.KDA_N, wl.KDA_K)])
 def test_full_shape_exact_sum_every_planned_tactic(N, K):

@@ -50,13 +50,19 @@ const Entry kTable[] = {
 }  // namespace
 
 bool lookup_measured_tactic(int N, int K, int bin, proj_tactic_t *out) {
+    // The smallest measured bin at or above `bin` for the shape: its tactic
+    // serves any batch up to its capacity, so a plan's own bins (say the
+    // verify batches 3, 6, 12 of speculative decoding) take the measured
+    // choice of the next power of two above them.
+    const Entry *best = nullptr;
     for (const Entry &e : kTable) {
-        if (e.N == N && e.K == K && e.bin == bin && e.t.kernel != 0) {
-            *out = e.t;
-            return true;
-        }
+        if (e.N == N && e.K == K && e.bin >= bin && e.t.kernel != 0 &&
+            (!best || e.bin < best->bin))
+            best = &e;
     }
-    return false;
+    if (!best) return false;
+    *out = best->t;
+    return true;
 }
 
 }  // namespace tp1

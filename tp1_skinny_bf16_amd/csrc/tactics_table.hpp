@@ -5,8 +5,9 @@
 
 namespace tp1 {
 
-// Exact (N, K, bin) lookup in the table measured on MI355X.  Returns false
-// when the shape/bin was not measured.
+// Lookup in the table measured on MI355X: the tactic of the smallest
+// measured bin >= bin for (N, K).  Returns false when the shape was not
+// measured or every measured bin is below `bin`.
 bool lookup_measured_tactic(int N, int K, int bin, proj_tactic_t *out);
 
 }  // namespace tp1

@@ -35,6 +35,9 @@ def _args():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--report", default=None, help="write the all-config report here")
+    ap.add_argument("--configs", default=None,
+                    help="with --report: comma-separated configuration names to time "
+                         "(default all, with the read ceiling and the multi-layer chain)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall time of the bounded oracle sample (whole steps)")
@@ -181,19 +184,24 @@ def report(args, torch, tp, wl, timing):
     """Every configuration point, cold (rotated weights) and hot."""
     dev = torch.device("cuda:0")
     out = {"points": [], "device": torch.cuda.get_device_name(0)}
-    # plain streaming-read ceiling over a 2 GB buffer
-    buf = torch.empty(2 * 1024 ** 3 // 2, dtype=torch.bfloat16, device=dev)
-    buf.fill_(1.0)
-    sink = torch.empty(65536, dtype=torch.float32, device=dev)
-    probe = {}
-    for wpc in (4, 8, 16, 32):
-        r = timing.time_calls([lambda: tp.read_probe(buf, sink, wpc)], warmup=3, reps=20)
-        probe[wpc] = round(timing.gbs(buf.numel() * 2, r["us_median"]), 1)
-    out["read_ceiling_GBps"] = probe
-    _say(f"read ceiling (GB/s by waves/CU): {probe}")
-    del buf
+    names = set(args.configs.split(",")) if args.configs else None
+    unknown = (names or set()) - set(wl.BY_NAME)
+    if unknown:
+        raise SystemExit(f"unknown configurations: {sorted(unknown)}")
+    if names is None:
+        # plain streaming-read ceiling over a 2 GB buffer
+        buf = torch.empty(2 * 1024 ** 3 // 2, dtype=torch.bfloat16, device=dev)
+        buf.fill_(1.0)
+        sink = torch.empty(65536, dtype=torch.float32, device=dev)
+        probe = {}
+        for wpc in (4, 8, 16, 32):
+            r = timing.time_calls([lambda: tp.read_probe(buf, sink, wpc)], warmup=3, reps=20)
+            probe[wpc] = round(timing.gbs(buf.numel() * 2, r["us_median"]), 1)
+        out["read_ceiling_GBps"] = probe
+        _say(f"read ceiling (GB/s by waves/CU): {probe}")
+        del buf
     for cfg in wl.CONFIGS:
-        if cfg.layers > 1:
+        if cfg.layers > 1 or (names is not None and cfg.name not in names):
             continue
         t = wl.config_tensors(cfg)
         W0 = t["W"].to(dev)
@@ -221,6 +229,10 @@ def report(args, torch, tp, wl, timing):
                  f"{p['pct_peak']:5.1f}% hot {p['hot_us']:7.2f} us  {p['kernel']}")
         del copies, W0, x, t
         torch.cuda.empty_cache()
+    if names is not None and "multilayer" not in names:
+        with open(args.report, "w") as f:
+            json.dump(out, f, indent=1)
+        return
     # multi-layer stream: 8 x (in-proj 14560x7168 -> o_proj 7168x12288), B = 64
     cfg = wl.BY_NAME["multilayer"]
     g = torch.Generator(device=dev)
@@ -250,9 +262,9 @@ def report(args, torch, tp, wl, timing):
 def main():
     args = _args()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU only: the projection "
-                          "runs on one GPU's share (one DEP rank) and nothing here "
-                          "shards or communicates; run with --gpus 1"}))
+        print(json.dumps({"error": "the projection is measured on one GPU: it runs one "
+                          "DEP rank's share, and this library neither shards nor "
+                          "communicates across GPUs; run with --gpus 1"}))
         sys.exit(2)
     import torch
 
@@ -264,6 +276,11 @@ def main():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
     torch.cuda.set_device(0)
+    if args.report and args.configs:
+        # a report of selected configurations only (e.g. under a counter run):
+        # no headline steps, so every dispatch belongs to the named points
+        report(args, torch, tp, wl, timing)
+        return
     h = headline(args, torch, tp, wl, timing)
     cpu = None
     if not args.no_cpu:

@@ -896,14 +896,17 @@ __global__ __launch_bounds__(256) void mfma_xs_kernel(MfmaArgs a) {
 // One barrier per chunk.
 //
 // LDS layout of a stage: rows of KC/8 16-byte pieces, x rows first, then
-// weight rows; piece p of row r sits at position (p + (r >> SH)) mod (KC/8)
-// of its row, a rotation that puts the 16 rows of an MFMA fragment read in
-// 16 distinct bank groups without padding.  One load instruction fills 1 KB
-// of consecutive positions (64 lanes x 16 bytes), so each lane loads the
-// global piece that lands in its position.  Pieces past the slice end, batch
-// rows past B and weight rows past the workgroup's rows load 16 zero bytes
-// instead (zero x or weight pieces add nothing; the rows' outputs are never
-// stored).
+// weight rows; piece p of row r sits at position p ^ q(r) of its row, with
+// q(r) = r mod (KC/8) for rows of 8 or more pieces and (r >> 1) mod 4 for
+// rows of 4.  Measured bank-conflict counts of 128-bit LDS reads on gfx950
+// fit 64 four-byte banks served eight lanes (two groups of four) at a time;
+// with this swizzle the fragment reads count zero conflicts at every chunk
+// width, where a rotation p + r leaves a 2-way conflict, and no row is
+// padded.  One load instruction fills 1 KB of consecutive positions (64
+// lanes x 16 bytes), so each lane loads the global piece that lands in its
+// position.  Pieces past the slice end, batch rows past B and weight rows
+// past the workgroup's rows load 16 zero bytes instead (zero x or weight
+// pieces add nothing; the rows' outputs are never stored).
 //
 // The direct-to-LDS loads are issued from inline assembly, so the compiler
 // does not track them: the wait for a stage is an explicit vmcnt wait for
@@ -946,7 +949,6 @@ __global__ __launch_bounds__(NWV * 64) void mfma_pipe_kernel(MfmaArgs a) {
     constexpr int XR = 16 * MT;                  // x rows per stage
     constexpr int GR = 16 * NTB;                 // weight rows per group
     constexpr int PP = KC / 8;                   // 16-byte pieces per row
-    constexpr int SH = PP >= 16 ? 0 : (PP == 8 ? 1 : 2);
     constexpr int STAGE = (XR + GR) * PP * 16;   // bytes per stage
     constexpr int NB = (XR + GR) * PP / 64;      // 1 KB load blocks per stage
     constexpr int XB = XR * PP / 64;             // of which x blocks
@@ -980,13 +982,15 @@ __global__ __launch_bounds__(NWV * 64) void mfma_pipe_kernel(MfmaArgs a) {
 
     // This lane's piece of each of the wave's load blocks: stage row r and
     // piece p (its K offset within the chunk is 8 * p).
+    // The swizzle is its own inverse: position v of row r holds piece v ^ q(r).
+    auto swz = [](int r) { return PP == 4 ? (r >> 1) & 3 : r & (PP - 1); };
     int lr[NI], lpk[NI];
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
         const int slot = (i * NWV + wave) * 64 + lane;
         const int r = slot / PP;
         lr[i] = r;
-        lpk[i] = (((slot % PP) - (r >> SH)) & (PP - 1)) * 8;
+        lpk[i] = ((slot % PP) ^ swz(r)) * 8;
     }
 
     int it = 0, ig = 0, ic = 0;  // the next step to load
@@ -1045,13 +1049,13 @@ __global__ __launch_bounds__(NWV * 64) void mfma_pipe_kernel(MfmaArgs a) {
             for (int n = 0; n < NTW; ++n) {
                 const int r = XR + (wn * NTW + n) * 16 + lrow;
                 bf[n] = *reinterpret_cast<const u32x4 *>(
-                    stg + (r * PP + ((p + (r >> SH)) & (PP - 1))) * 16);
+                    stg + (r * PP + (p ^ swz(r))) * 16);
             }
 #pragma unroll
             for (int m = 0; m < MTW; ++m) {
                 const int r = (wm * MTW + m) * 16 + lrow;
                 const u32x4 af = *reinterpret_cast<const u32x4 *>(
-                    stg + (r * PP + ((p + (r >> SH)) & (PP - 1))) * 16);
+                    stg + (r * PP + (p ^ swz(r))) * 16);
 #pragma unroll
                 for (int n = 0; n < NTW; ++n)
                     acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(

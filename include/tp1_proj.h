@@ -105,6 +105,13 @@ enum proj_kernel {
  *            workgroup split each chunk's K steps kw ways and add their
  *            partial tiles in LDS in a fixed order; 0 elsewhere
  *   nw     : MFMA_PIPE: waves per workgroup (4 or 8); 0 elsewhere
+ *   stagger: MFMA_XS, MFMA_PIPE: 1 = workgroup b walks its slice's K chunks
+ *            starting at chunk b mod C (C chunks) and wrapping, so the
+ *            workgroups' reads in flight are spread over K instead of all
+ *            sitting at the same column of their rows; 0 = every workgroup
+ *            starts at the first chunk.  The summation order then depends
+ *            on the workgroup index only, so results stay reproducible.
+ *            0 elsewhere
  */
 typedef struct proj_tactic {
     int kernel;
@@ -117,6 +124,7 @@ typedef struct proj_tactic {
     int depth;
     int kw;
     int nw;
+    int stagger;
 } proj_tactic_t;
 
 typedef struct proj_plan_s proj_plan_t;

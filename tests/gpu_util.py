@@ -114,6 +114,9 @@ def candidate_tactics(N: int, K: int, bin_: int):
             for split in (1, 3):
                 for wpc in (1, 2):
                     out.append(tp.Tactic(tp.KERNEL_MFMA_XS, bc, split, rows, waves, wpc, kc, depth))
+                    if wpc == 1:  # the same with a staggered chunk order
+                        out.append(tp.Tactic(tp.KERNEL_MFMA_XS, bc, split, rows, waves, wpc, kc,
+                                             depth, stagger=1))
     pipe = {16: ((4, 1, 1, 128, 3, 4), (4, 1, 1, 128, 4, 4), (4, 1, 1, 128, 6, 4),
                  (4, 1, 1, 256, 3, 4), (8, 1, 1, 128, 3, 4), (8, 1, 1, 128, 4, 4),
                  (2, 1, 2, 256, 6, 4), (2, 1, 2, 256, 4, 4), (2, 1, 2, 128, 8, 4),
@@ -141,6 +144,9 @@ def candidate_tactics(N: int, K: int, bin_: int):
                 for wpc in (1, 2):
                     out.append(tp.Tactic(tp.KERNEL_MFMA_PIPE, bc, split, rows, waves, wpc, kc,
                                          depth, kw, nw))
+                    if wpc == 1:  # the same with a staggered chunk order
+                        out.append(tp.Tactic(tp.KERNEL_MFMA_PIPE, bc, split, rows, waves, wpc,
+                                             kc, depth, kw, nw, stagger=1))
     for bc in (16, 32, 64, 128, 256):
         if bc < bin_:
             continue

@@ -193,6 +193,23 @@ def test_unlisted_bins_take_the_next_measured_tactic():
     assert r.tactic(1)[0].kernel in tp.KERNEL_NAMES
 
 
+def test_stagger_is_validated():
+    p = tp.Plan(14560, 7168, [1, 16], host_only=True)
+    for ok in [tp.Tactic(tp.KERNEL_MFMA_PIPE, 16, 1, 4, 1, 1, 256, 3, 2, 8, stagger=1),
+               tp.Tactic(tp.KERNEL_MFMA_XS, 16, 1, 8, 1, 2, 128, 1, stagger=1)]:
+        p.set_tactic(16, ok)
+        assert p.tactic(16)[0] == ok
+    for bin_, bad in [(16, tp.Tactic(tp.KERNEL_MFMA_PIPE, 16, 1, 4, 1, 1, 256, 3, 2, 8,
+                                     stagger=2)),
+                      (16, tp.Tactic(tp.KERNEL_MFMA_PIPE, 16, 1, 4, 1, 1, 256, 3, 2, 8,
+                                     stagger=-1)),
+                      (16, tp.Tactic(tp.KERNEL_MFMA_LDS, 16, 1, 1, 2, 4, stagger=1)),
+                      (16, tp.Tactic(tp.KERNEL_MFMA, 16, 1, 2, 4, 0, stagger=1)),
+                      (1, tp.Tactic(tp.KERNEL_STREAM, 1, 1, 4, 4, 8, stagger=1))]:
+        with pytest.raises(tp.ProjError):
+            p.set_tactic(bin_, bad)
+
+
 def test_pipe_only_fields_are_validated():
     p = tp.Plan(14560, 7168, [16], host_only=True)
     ok = tp.Tactic(tp.KERNEL_MFMA_PIPE, 16, 1, 4, 1, 1, 256, 3, 2, 8)

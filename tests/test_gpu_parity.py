@@ -268,7 +268,9 @@ def test_fused_split_matches_two_pass_bitwise():
                (16, tp.Tactic(tp.KERNEL_MFMA_PIPE, 16, 4, 4, 1, 2, 128, 4, 1, 4)),
                (16, tp.Tactic(tp.KERNEL_MFMA_PIPE, 16, 2, 2, 1, 1, 256, 4, 2, 4)),
                (64, tp.Tactic(tp.KERNEL_MFMA_PIPE, 64, 3, 8, 2, 2, 64, 4, 1, 4)),
-               (64, tp.Tactic(tp.KERNEL_MFMA_PIPE, 64, 4, 16, 2, 1, 64, 3, 1, 8))]
+               (64, tp.Tactic(tp.KERNEL_MFMA_PIPE, 64, 4, 16, 2, 1, 64, 3, 1, 8)),
+               (16, tp.Tactic(tp.KERNEL_MFMA_PIPE, 16, 3, 2, 1, 1, 256, 4, 4, 8, stagger=1)),
+               (64, tp.Tactic(tp.KERNEL_MFMA_XS, 64, 2, 4, 2, 1, 128, 2, stagger=1))]
     for bin_, t in tactics:
         fused.set_tactic(bin_, t)
         twop.set_tactic(bin_, t)

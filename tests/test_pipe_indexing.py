@@ -199,6 +199,23 @@ def test_loader_and_reader_agree(inst):
                 assert (wm * g.MTW + m) * 16 + 15 < g.XR
 
 
+def rotated_chunk(ic, bx, C, stagger):
+    """Chunk a workgroup loads at its chunk step ic (the kernel's stagger rule)."""
+    c0 = bx % C if stagger else 0
+    return ic + c0 if ic + c0 < C else ic + c0 - C
+
+
+@pytest.mark.parametrize("C", [1, 2, 7, 48, 56, 96])
+def test_staggered_chunk_order_is_a_rotation(C):
+    # Every workgroup still loads each chunk of its slice once, within 0..C-1,
+    # so the extreme chunks the bounds test below checks are the same.
+    for bx in (0, 1, C - 1, C, 255, 511):
+        for stagger in (0, 1):
+            order = [rotated_chunk(ic, bx, C, stagger) for ic in range(C)]
+            assert sorted(order) == list(range(C))
+            assert order[0] == (bx % C if stagger else 0)
+
+
 def _slices(K, KC, split):
     step = max(KC, 32)
     ks = max(ceil(ceil(K, split), step) * step, step)

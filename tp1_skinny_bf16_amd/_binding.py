@@ -56,7 +56,8 @@ class _Tactic(ctypes.Structure):
     _fields_ = [("kernel", ctypes.c_int), ("bcap", ctypes.c_int),
                 ("split", ctypes.c_int), ("rows", ctypes.c_int),
                 ("waves", ctypes.c_int), ("wpc", ctypes.c_int), ("kc", ctypes.c_int),
-                ("depth", ctypes.c_int), ("kw", ctypes.c_int), ("nw", ctypes.c_int)]
+                ("depth", ctypes.c_int), ("kw", ctypes.c_int), ("nw", ctypes.c_int),
+                ("stagger", ctypes.c_int)]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -71,6 +72,7 @@ class Tactic:
     depth: int = 0
     kw: int = 0
     nw: int = 0
+    stagger: int = 0
 
     @property
     def kernel_name(self) -> str:
@@ -83,7 +85,7 @@ class Tactic:
 
     def _c(self) -> _Tactic:
         return _Tactic(self.kernel, self.bcap, self.split, self.rows, self.waves,
-                       self.wpc, self.kc, self.depth, self.kw, self.nw)
+                       self.wpc, self.kc, self.depth, self.kw, self.nw, self.stagger)
 
 
 _LIB = None
@@ -200,7 +202,7 @@ class Plan:
         _check(_lib().proj_plan_tactic(self._h, int(B), ctypes.byref(t), ctypes.byref(b)),
                f"proj_plan_tactic(B={B})")
         return (Tactic(t.kernel, t.bcap, t.split, t.rows, t.waves, t.wpc, t.kc, t.depth, t.kw,
-                       t.nw), b.value)
+                       t.nw, t.stagger), b.value)
 
     def kernel_name(self, B: int) -> str:
         """Kernel instance(s) proj_run launches for batch B (profiler names)."""

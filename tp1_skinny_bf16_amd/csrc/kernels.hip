@@ -399,6 +399,7 @@ struct MfmaArgs {
     int N, K, B;
     int ks;    // K elements per slice (multiple of 32)
     int S;
+    int stagger;  // 1: workgroup b starts at chunk b mod C of its slice (XS, PIPE)
 };
 
 template <int MT, int NT, int P>
@@ -745,7 +746,8 @@ __global__ __launch_bounds__(256) void mfma_lds_kernel(MfmaArgs a) {
 // and reuses each fragment across them.  The next one or two chunks are
 // loaded into registers while this one is multiplied; two barriers per chunk.  LDS rows
 // are padded by 16 bytes so the 16 rows of a fragment read fall in distinct
-// banks.
+// banks.  The stagger option rotates the chunk order per workgroup as in
+// mfma_pipe_kernel below.
 // ---------------------------------------------------------------------------
 template <int MT, int NTB, int WM, int kXsChunk, int PD>
 __global__ __launch_bounds__(256) void mfma_xs_kernel(MfmaArgs a) {
@@ -800,9 +802,11 @@ __global__ __launch_bounds__(256) void mfma_xs_kernel(MfmaArgs a) {
     // grid, never stored), so every round issues the same loads.  The offset,
     // not the base pointer, is selected: a pointer select becomes a branch.
     int lt = 0, lg = 0, lc = 0;
+    const int c0 = a.stagger ? (int)(blockIdx.x % (unsigned)C) : 0;
+    auto rotated = [&](int c) { return c + c0 < C ? c + c0 : c + c0 - C; };
     auto load_chunk = [&](u32x4 (&xx)[XV], u32x4 (&ww)[WV]) {
         const size_t live = lt < T ? 1 : 0;
-        const int kk = min(lc * kXsChunk + pk, klen - 8);
+        const int kk = min(rotated(lc) * kXsChunk + pk, klen - 8);
 #pragma unroll
         for (int i = 0; i < XV; ++i) {
             const int b = min(i * RPS + prow, a.B - 1);
@@ -841,7 +845,7 @@ __global__ __launch_bounds__(256) void mfma_xs_kernel(MfmaArgs a) {
         for (int p = 0; p < PD; ++p) {
             if (t0 + p < T) {                // uniform
                 __syncthreads();             // every wave is done with the previous tiles
-                store_chunk(xr[p], wr[p], c);
+                store_chunk(xr[p], wr[p], rotated(c));
                 __syncthreads();             // tiles of this step visible
                 load_chunk(xr[p], wr[p]);    // the step PD ahead into this set
                 __builtin_amdgcn_sched_barrier(0);   // all loads issue before the MFMAs
@@ -894,6 +898,13 @@ __global__ __launch_bounds__(256) void mfma_xs_kernel(MfmaArgs a) {
 // ring of D stages, D-1 chunks ahead of the one being multiplied, so the
 // loads in flight do not hold registers and no wave copies data into LDS.
 // One barrier per chunk.
+//
+// Chunk order: with the stagger option workgroup b walks the chunks of its
+// slice from chunk b mod C and wraps.  Without it every workgroup reads the
+// same K columns at the same time, and when the row pitch is a multiple of a
+// few KB those addresses share their low bits across the whole grid; spread
+// over K they load the memory channels more evenly (measured on the
+// 7168 x 12288 shape: the slowest workgroups finish ~2 us sooner).
 //
 // LDS layout of a stage: rows of KC/8 16-byte pieces, x rows first, then
 // weight rows; piece p of row r sits at position p ^ q(r) of its row, with
@@ -994,13 +1005,15 @@ __global__ __launch_bounds__(NWV * 64) void mfma_pipe_kernel(MfmaArgs a) {
     }
 
     int it = 0, ig = 0, ic = 0;  // the next step to load
+    const int c0 = a.stagger ? (int)(blockIdx.x % (unsigned)C) : 0;
     auto issue = [&]() {
         const uint32_t st = lds0 + (uint32_t)((it % D) * STAGE);
         const bool live = it < T;  // uniform; past the end only zeros load
+        const int cc = ic + c0 < C ? ic + c0 : ic + c0 - C;  // chunk loaded
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
             const int bi = i * NWV + wave;
-            const int k = ic * KC + lpk[i];
+            const int k = cc * KC + lpk[i];
             const uint32_t m0 = st + (uint32_t)bi * 1024u;
             if (bi < XB) {
                 const int b = lr[i];
@@ -1293,7 +1306,7 @@ hipError_t launch_mfma_xs_inst(const LaunchShape &sh, const proj_tactic_t &t,
         lds_allowed = lds;
     }
     MfmaArgs a{sh.x, sh.ldx, sh.W, sh.y, sh.ws, fused_counters(sh, g, S), sh.N, sh.K, sh.B,
-               ks, S};
+               ks, S, t.stagger};
     hipLaunchKernelGGL((mfma_xs_kernel<MT, NTB, WM, KC, PD>), dim3((unsigned)g, S), dim3(256), lds,
                        stream, a);
     return hipGetLastError();
@@ -1326,7 +1339,7 @@ hipError_t launch_mfma_pipe_inst(const LaunchShape &sh, const proj_tactic_t &t,
         lds_allowed = lds;
     }
     MfmaArgs a{sh.x, sh.ldx, sh.W, sh.y, sh.ws, fused_counters(sh, g, S), sh.N, sh.K, sh.B,
-               ks, S};
+               ks, S, t.stagger};
     hipLaunchKernelGGL((mfma_pipe_kernel<MT, NTB, WM, WK, KC, D, NWV>), dim3((unsigned)g, S),
                        dim3(NWV * 64), lds, stream, a);
     return hipGetLastError();

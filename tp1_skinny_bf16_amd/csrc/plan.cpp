@@ -157,6 +157,9 @@ int check_tactic(int N, int K, int bin, const proj_tactic_t &t) {
         return PROJ_EINVAL;
     }
     if (t.kernel != PROJ_KERNEL_MFMA_PIPE && (t.kw != 0 || t.nw != 0)) return PROJ_EINVAL;
+    if (t.stagger != 0 && t.stagger != 1) return PROJ_EINVAL;
+    if (t.stagger && t.kernel != PROJ_KERNEL_MFMA_XS && t.kernel != PROJ_KERNEL_MFMA_PIPE)
+        return PROJ_EINVAL;
     return PROJ_OK;
 }
 

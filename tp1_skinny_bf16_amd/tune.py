@@ -69,6 +69,9 @@ def candidates(bin_: int, full: bool = False):
           128: ((4, 2, 128, 1), (4, 4, 128, 1)), 256: ((4, 4, 128, 1), (2, 4, 128, 1))}[bc]
     for (rows, waves, kc, depth), split, wpc in itertools.product(xs, (1, 2, 3, 4), (1, 2)):
         out.append(Tactic(KERNEL_MFMA_XS, bc, split, rows, waves, wpc, kc, depth))
+        if split <= 2:
+            out.append(Tactic(KERNEL_MFMA_XS, bc, split, rows, waves, wpc, kc, depth,
+                              stagger=1))
     pipe = {16: ((4, 1, 1, 128, 3, 4), (4, 1, 1, 128, 4, 4), (4, 1, 1, 128, 6, 4),
                  (4, 1, 1, 256, 3, 4), (8, 1, 1, 128, 3, 4), (8, 1, 1, 128, 4, 4),
                  (2, 1, 2, 256, 6, 4), (2, 1, 2, 256, 4, 4), (2, 1, 2, 128, 8, 4),
@@ -93,6 +96,9 @@ def candidates(bin_: int, full: bool = False):
         if (split > 4 and bc < 64) or (nw == 8 and wpc > 1):
             continue
         out.append(Tactic(KERNEL_MFMA_PIPE, bc, split, rows, waves, wpc, kc, depth, kw, nw))
+        if split in (1, 2, 4):
+            out.append(Tactic(KERNEL_MFMA_PIPE, bc, split, rows, waves, wpc, kc, depth, kw, nw,
+                              stagger=1))
     return out
 
 
@@ -181,7 +187,8 @@ def table_rows(result) -> str:
              "mfma_pipe": "PROJ_KERNEL_MFMA_PIPE"}[t["kernel"]]
         lines.append(f"    {{{result['N']}, {result['K']}, {b}, {{{k}, {t['bcap']}, {t['split']}, "
                      f"{t['rows']}, {t['waves']}, {t['wpc']}, {t.get('kc', 0)}, "
-                     f"{t.get('depth', 0)}, {t.get('kw', 0)}, {t.get('nw', 0)}}}}},  // "
+                     f"{t.get('depth', 0)}, {t.get('kw', 0)}, {t.get('nw', 0)}, "
+                     f"{t.get('stagger', 0)}}}}},  // "
                      f"{r['chosen']['us']} us, {r['GBps']} GB/s")
     return "\n".join(lines)
 
@@ -225,7 +232,8 @@ def summarize(paths) -> str:
     for (N, K) in sorted({(n, k) for n, k, _ in chosen}):
         bins = sorted(b for n, k, b in chosen if (n, k) == (N, K))
         lines += [f"## {N} x {K}", "",
-                  "| bin | chosen kernel | tactic (bcap, split, rows, waves, wpc, kc, depth, kw, nw) "
+                  "| bin | chosen kernel | tactic (bcap, split, rows, waves, wpc, kc, depth, kw, nw, "
+                  "stagger) "
                   "| us "
                   "| GB/s "
                   "| best stream us | best MFMA us | candidates |",
@@ -238,7 +246,7 @@ def summarize(paths) -> str:
                 cross = b
             lines.append(f"| {b} | `{r['chosen']['kernel']}` | {t['bcap']}, {t['split']}, {t['rows']}, "
                          f"{t['waves']}, {t['wpc']}, {t.get('kc', 0)}, {t.get('depth', 0)}, "
-                         f"{t.get('kw', 0)}, {t.get('nw', 0)} | "
+                         f"{t.get('kw', 0)}, {t.get('nw', 0)}, {t.get('stagger', 0)} | "
                          f"{r['chosen']['us']} | {r['GBps']} | "
                          f"{r.get('best_stream_us')} | {r.get('best_mfma_us')} | {r['n_candidates']} |")
         lines += ["", f"Crossover (first bin whose best tactic is an MFMA kernel): {cross}", ""]

@@ -34,6 +34,9 @@ def _args():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warm-seconds", type=float, default=0.3,
+                    help="after the warmup steps, keep stepping (untimed) until this much "
+                         "time has passed, so the timed steps do not run at ramping clocks")
     ap.add_argument("--report", default=None, help="write the all-config report here")
     ap.add_argument("--configs", default=None,
                     help="with --report: comma-separated configuration names to time "
@@ -90,6 +93,15 @@ def headline(args, torch, tp, wl, timing):
 
     for s in range(args.warmup):
         step(s)
+    # A fresh process starts at low clocks; a few ms of warm-up steps do not
+    # raise them.  Keep stepping, untimed, until warm_seconds have passed.
+    t_warm = time.perf_counter()
+    s = args.warmup
+    while time.perf_counter() - t_warm < args.warm_seconds:
+        for _ in range(20):
+            step(s)
+            s += 1
+        torch.cuda.synchronize()
     # Timed region: the K steps' calls, grouped by batch size (B-major) so that
     # each size's K calls run back to back between one pair of HIP events on
     # the launch stream; a step is still one call per batch size.
@@ -298,6 +310,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "warm_seconds": args.warm_seconds,
         "ms_per_step": round(h["ms"], 4),
         "higher_is_better": True,
         "scaling": "weak",

@@ -265,6 +265,22 @@ def report(args, torch, tp, wl, timing):
                          "GBps": round(timing.gbs(nbytes, r["us_median"]), 1),
                          "bytes": nbytes, "in_kernel": pin.kernel_name(cfg.bmax),
                          "o_kernel": po.kernel_name(cfg.bmax)}
+    # the same chain captured once as a graph and replayed (the launches of
+    # all 2 x 8 projections, split-K passes included, submitted as one)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        stack.run(x0, y_in, y_o)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        stack.run(x0, y_in, y_o)
+    torch.cuda.synchronize()
+    rg = timing.time_calls([graph.replay], warmup=3, reps=20)
+    out["multilayer"].update({"graph_us_median": round(rg["us_median"], 1),
+                              "graph_GBps": round(timing.gbs(nbytes, rg["us_median"]), 1)})
+    del graph
     _say(f"multilayer 8x(in+o) B=64: {out['multilayer']}")
     with open(args.report, "w") as f:
         json.dump(out, f, indent=1)

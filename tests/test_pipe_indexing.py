@@ -251,14 +251,19 @@ def test_global_loads_in_bounds(inst):
                             rows = N * (bx + 1) // grid - row0
                             assert rows >= 1
                             T = ceil(rows, g.GR) * C
-                            for it in sorted({0, C - 1, T - C, T - 1}):
+                            # the last D-1 steps are the ring's loads past the end
+                            for it in sorted({0, C - 1, T - C, T - 1, T + g.D - 2}):
                                 ig, ic = it // C, it % C
                                 k = ic * g.KC + kp
                                 live_k = k < klen          # else the zero block loads
-                                xl = is_x & live_k & (r < B)
-                                assert np.all(r[xl] * K + k0 + k[xl] + 8 <= B * K)
-                                rr = ig * g.GR + r - g.XR
-                                wl = ~is_x & live_k & (rr < rows)
+                                # rows past B repeat row B-1; weight rows past
+                                # the range (and past the last step) repeat the
+                                # range's last row
+                                xl = is_x & live_k
+                                b = np.minimum(r, B - 1)
+                                assert np.all(b[xl] * K + k0 + k[xl] + 8 <= B * K)
+                                rr = np.minimum(ig * g.GR + r - g.XR, rows - 1)
+                                wl = ~is_x & live_k
                                 assert np.all(row0 + rr[wl] < N)
                                 assert np.all(k0 + k[wl] + 8 <= K)
                                 assert np.all(rr[wl] >= 0)

@@ -915,9 +915,10 @@ __global__ __launch_bounds__(256) void mfma_xs_kernel(MfmaArgs a) {
 // width, where a rotation p + r leaves a 2-way conflict, and no row is
 // padded.  One load instruction fills 1 KB of consecutive positions (64
 // lanes x 16 bytes), so each lane loads the global piece that lands in its
-// position.  Pieces past the slice end, batch rows past B and weight rows
-// past the workgroup's rows load 16 zero bytes instead (zero x or weight
-// pieces add nothing; the rows' outputs are never stored).
+// position.  Pieces past the slice end load 16 zero bytes instead (they meet
+// live rows, so they must add nothing); batch rows past B and weight rows
+// past the workgroup's rows repeat a live row (their outputs are never
+// stored).
 //
 // The direct-to-LDS loads are issued from inline assembly, so the compiler
 // does not track them: the wait for a stage is an explicit vmcnt wait for
@@ -1008,24 +1009,28 @@ __global__ __launch_bounds__(NWV * 64) void mfma_pipe_kernel(MfmaArgs a) {
     const int c0 = a.stagger ? (int)(blockIdx.x % (unsigned)C) : 0;
     auto issue = [&]() {
         const uint32_t st = lds0 + (uint32_t)((it % D) * STAGE);
-        const bool live = it < T;  // uniform; past the end only zeros load
         const int cc = ic + c0 < C ? ic + c0 : ic + c0 - C;  // chunk loaded
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
             const int bi = i * NWV + wave;
             const int k = cc * KC + lpk[i];
             const uint32_t m0 = st + (uint32_t)bi * 1024u;
+            // Batch rows past B repeat row B-1, and weight rows past the
+            // range (all of them in the ring's steps past the last one)
+            // repeat the last row: they only feed outputs that are never
+            // stored, and real addresses spread these loads over the memory
+            // channels like the live ones (a single shared address would
+            // queue them all on one).  Only pieces past the slice end must
+            // be zero, since they meet live rows.
             if (bi < XB) {
-                const int b = lr[i];
-                const bool ok = live && k < klen && b < a.B;
+                const int b = min(lr[i], a.B - 1);
                 const uint16_t *src =
-                    ok ? a.x + (size_t)b * a.ldx + k0 + k : kZeroPiece;
+                    k < klen ? a.x + (size_t)b * a.ldx + k0 + k : kZeroPiece;
                 lds_load16_cached(src, m0);
             } else {
-                const int r = ig * GR + lr[i] - XR;
-                const bool ok = live && k < klen && r < rows;
+                const int r = min(ig * GR + lr[i] - XR, rows - 1);
                 const uint16_t *src =
-                    ok ? a.W + (size_t)(row0 + r) * a.K + k0 + k : kZeroPiece;
+                    k < klen ? a.W + (size_t)(row0 + r) * a.K + k0 + k : kZeroPiece;
                 lds_load16_stream(src, m0);
             }
         }
@@ -1132,6 +1137,24 @@ __global__ __launch_bounds__(256) void splitk_reduce(const float *ws, uint16_t *
     float acc = ws[i];
     for (int s = 1; s < S; ++s) acc += ws[(size_t)s * count + i];
     y[i] = to_bf16(acc);
+}
+
+// The same sum four outputs per thread (count % 4 == 0): one 16-byte load
+// per slice and one 8-byte store, each output still added s = 0..S-1.
+__global__ __launch_bounds__(256) void splitk_reduce4(const f32x4 *ws, uint2 *y, long count4,
+                                                      int S) {
+    const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= count4) return;
+    f32x4 acc = __builtin_nontemporal_load(ws + i);
+    for (int s = 1; s < S; ++s) {
+        const f32x4 v = __builtin_nontemporal_load(ws + (size_t)s * count4 + i);
+        acc.x += v.x;
+        acc.y += v.y;
+        acc.z += v.z;
+        acc.w += v.w;
+    }
+    y[i] = make_uint2((unsigned)to_bf16(acc.x) | ((unsigned)to_bf16(acc.y) << 16),
+                      (unsigned)to_bf16(acc.z) | ((unsigned)to_bf16(acc.w) << 16));
 }
 
 // ---------------------------------------------------------------------------
@@ -1405,8 +1428,13 @@ hipError_t launch_projection(const LaunchShape &sh, const proj_tactic_t &t,
     const int S = slice_count(sh.K, t);
     if (S > 1 && !fused_counters(sh, grid_x(sh, t), S)) {
         const long count = (long)sh.B * sh.N;
-        hipLaunchKernelGGL(splitk_reduce, dim3(ceil_div_i(count, 256)), dim3(256), 0,
-                           stream, sh.ws, sh.y, count, S);
+        if (count % 4 == 0)   // y is 16-byte aligned (proj_run checks it)
+            hipLaunchKernelGGL(splitk_reduce4, dim3(ceil_div_i(count / 4, 256)), dim3(256), 0,
+                               stream, reinterpret_cast<const f32x4 *>(sh.ws),
+                               reinterpret_cast<uint2 *>(sh.y), count / 4, S);
+        else
+            hipLaunchKernelGGL(splitk_reduce, dim3(ceil_div_i(count, 256)), dim3(256), 0,
+                               stream, sh.ws, sh.y, count, S);
         e = hipGetLastError();
     }
     return e;
@@ -1416,24 +1444,26 @@ int kernel_name(const LaunchShape &sh, const proj_tactic_t &t, char *buf, size_t
     if (!buf || len == 0) return -1;
     const int S = slice_count(sh.K, t);
     const bool split = S > 1 && !fused_counters(sh, grid_x(sh, t), S);
+    // the reduction pass launch_projection picks
+    const char *red = ((long)sh.B * sh.N) % 4 == 0 ? "+splitk_reduce4" : "+splitk_reduce";
     int n;
     if (t.kernel == PROJ_KERNEL_STREAM || t.kernel == PROJ_KERNEL_STREAM_DOT2)
         n = snprintf(buf, len, "stream_kernel<%d, %d, %d, %s>%s", t.bcap, t.rows,
                      stream_ring(t.bcap, t.rows),
                      t.kernel == PROJ_KERNEL_STREAM_DOT2 ? "true" : "false",
-                     split ? "+splitk_reduce" : "");
+                     split ? red : "");
     else if (t.kernel == PROJ_KERNEL_MFMA_LDS)
         n = snprintf(buf, len, "mfma_lds_kernel<%d, %d>%s", t.bcap / 16, t.rows,
-                     split ? "+splitk_reduce" : "");
+                     split ? red : "");
     else if (t.kernel == PROJ_KERNEL_MFMA_XS)
         n = snprintf(buf, len, "mfma_xs_kernel<%d, %d, %d, %d, %d>%s", t.bcap / 16, t.rows,
-                     t.waves, t.kc, t.depth, split ? "+splitk_reduce" : "");
+                     t.waves, t.kc, t.depth, split ? red : "");
     else if (t.kernel == PROJ_KERNEL_MFMA_PIPE)
         n = snprintf(buf, len, "mfma_pipe_kernel<%d, %d, %d, %d, %d, %d, %d>%s", t.bcap / 16,
-                     t.rows, t.waves, t.kw, t.kc, t.depth, t.nw, split ? "+splitk_reduce" : "");
+                     t.rows, t.waves, t.kw, t.kc, t.depth, t.nw, split ? red : "");
     else
         n = snprintf(buf, len, "mfma_kernel<%d, %d, %d>%s", t.bcap / 16, t.rows,
-                     mfma_ring(t.bcap / 16, t.rows), split ? "+splitk_reduce" : "");
+                     mfma_ring(t.bcap / 16, t.rows), split ? red : "");
     return (n < 0 || (size_t)n >= len) ? -1 : 0;
 }
 

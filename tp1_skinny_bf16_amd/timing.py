@@ -18,9 +18,11 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense BF16 MFMA peak, TFLOP/s
 
 
 def rotation_copies(W0: torch.Tensor, min_total_bytes: float = 1.0e9,
-                    max_copies: int = 8, seed: int = 1000):
+                    max_copies: int = 64, seed: int = 1000):
     """[W0] plus distinct copies, drawn on the device, until the copies hold
-    at least `min_total_bytes` (values: same distribution, N(0, 0.02))."""
+    at least `min_total_bytes` (values: same distribution, N(0, 0.02)).  A
+    small weight (a tensor-parallel shard of 13-100 MB) takes up to 64 copies,
+    so that even then the set is four times the 256 MB MALL."""
     copies = [W0]
     nbytes = W0.numel() * W0.element_size()
     g = torch.Generator(device=W0.device)

@@ -77,7 +77,9 @@ def candidates(bin_: int, full: bool = False):
                  (2, 1, 2, 256, 6, 4), (2, 1, 2, 256, 4, 4), (2, 1, 2, 128, 8, 4),
                  (1, 1, 4, 256, 4, 4), (1, 1, 4, 256, 6, 4), (8, 1, 1, 256, 2, 8),
                  (4, 1, 2, 256, 3, 8), (2, 1, 4, 256, 6, 8),
-                 (2, 1, 4, 256, 4, 8), (1, 1, 8, 256, 4, 8)),
+                 (2, 1, 4, 256, 4, 8), (1, 1, 8, 256, 4, 8), (2, 1, 4, 512, 3, 8),
+                 (2, 1, 4, 512, 2, 8), (1, 1, 8, 512, 4, 8), (2, 1, 4, 512, 3, 4),
+                 (1, 1, 8, 512, 3, 8)),
             32: ((4, 1, 1, 128, 4, 4), (4, 1, 1, 128, 6, 4), (4, 2, 1, 64, 8, 4),
                  (8, 2, 1, 128, 3, 4), (2, 1, 2, 256, 4, 4), (2, 2, 1, 256, 4, 4),
                  (8, 2, 1, 128, 3, 8), (2, 1, 4, 256, 4, 8)),

@@ -2,6 +2,9 @@
 compare with the CPU oracle on the same seeded inputs."""
 from __future__ import annotations
 
+import os
+import re
+
 import numpy as np
 import torch
 
@@ -11,6 +14,7 @@ import tp1_skinny_bf16_amd as tp
 import workloads as wl
 
 DEV = torch.device("cuda:0")
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 
 def say(*a):
@@ -82,6 +86,16 @@ def tactic_label(plan, B):
     return f"{t.kernel_name} bcap={t.bcap} S={t.split} rows={t.rows} waves={t.waves} wpc={t.wpc} bin={b}"
 
 
+def pipe_instances():
+    """The compiled pipelined-kernel instances, read from the library's
+    instance list (plan.hpp), so every compiled instance is tested."""
+    src = open(os.path.join(ROOT, "tp1_skinny_bf16_amd", "csrc", "plan.hpp")).read()
+    blk = src[src.index("TP1_PIPE_INSTANCES(X)"):]
+    blk = blk[:blk.index("\n\n")]
+    pat = r"X\((\d+), (\d+), (\d+), (\d+), (\d+), (\d+), (\d+)\)"
+    return [tuple(map(int, m)) for m in re.findall(pat, blk)]
+
+
 def candidate_tactics(N: int, K: int, bin_: int):
     """A spread of valid tactics for a bin (every family and split path)."""
     out = []
@@ -117,31 +131,17 @@ def candidate_tactics(N: int, K: int, bin_: int):
                     if wpc == 1:  # the same with a staggered chunk order
                         out.append(tp.Tactic(tp.KERNEL_MFMA_XS, bc, split, rows, waves, wpc, kc,
                                              depth, stagger=1))
-    pipe = {16: ((4, 1, 1, 128, 3, 4), (4, 1, 1, 128, 4, 4), (4, 1, 1, 128, 6, 4),
-                 (4, 1, 1, 256, 3, 4), (8, 1, 1, 128, 3, 4), (8, 1, 1, 128, 4, 4),
-                 (2, 1, 2, 256, 6, 4), (2, 1, 2, 256, 4, 4), (2, 1, 2, 128, 8, 4),
-                 (1, 1, 4, 256, 4, 4), (1, 1, 4, 256, 6, 4), (8, 1, 1, 256, 2, 8),
-                 (4, 1, 2, 256, 3, 8), (2, 1, 4, 256, 6, 8),
-                 (2, 1, 4, 256, 4, 8), (1, 1, 8, 256, 4, 8)),
-            32: ((4, 1, 1, 128, 4, 4), (4, 1, 1, 128, 6, 4), (4, 2, 1, 64, 8, 4),
-                 (8, 2, 1, 128, 3, 4), (2, 1, 2, 256, 4, 4), (2, 2, 1, 256, 4, 4),
-                 (8, 2, 1, 128, 3, 8), (2, 1, 4, 256, 4, 8)),
-            64: ((4, 2, 1, 64, 8, 4), (4, 2, 1, 128, 4, 4), (4, 4, 1, 64, 8, 4),
-                 (8, 2, 1, 64, 4, 4), (8, 2, 1, 64, 6, 4), (16, 2, 1, 64, 3, 8),
-                 (8, 2, 1, 128, 3, 8), (16, 1, 1, 64, 3, 8), (8, 4, 1, 128, 3, 8),
-                 (8, 2, 1, 64, 6, 8)),
-            128: ((4, 4, 1, 64, 6, 4), (4, 4, 1, 32, 12, 4), (8, 4, 1, 64, 4, 4),
-                  (8, 4, 1, 32, 8, 4), (16, 2, 1, 64, 3, 8), (8, 2, 1, 64, 4, 8),
-                  (16, 4, 1, 32, 4, 8), (8, 2, 1, 32, 8, 8), (16, 2, 1, 32, 6, 8)),
-            256: ((4, 4, 1, 32, 7, 4), (4, 4, 1, 64, 3, 4), (8, 4, 1, 32, 6, 4),
-                  (8, 4, 1, 64, 3, 4), (16, 4, 1, 32, 4, 8),
-                  (8, 4, 1, 64, 3, 8), (8, 8, 1, 64, 3, 8), (8, 4, 1, 32, 6, 8))}
+    # every compiled pipelined instance: X(bcap, rows, waves, kw, kc, depth, nw)
+    pipe = {}
+    for (bc, rows, waves, kw, kc, depth, nw) in pipe_instances():
+        pipe.setdefault(bc, []).append((rows, waves, kw, kc, depth, nw))
     for bc, shapes in pipe.items():
-        if bc < bin_:
+        # each instance at the bins it would serve: capacity / 2 < bin <= capacity
+        if bc < bin_ or (bc > 16 and 2 * bin_ <= bc):
             continue
         for (rows, waves, kw, kc, depth, nw) in shapes:
             for split in (1, 3):
-                for wpc in (1, 2):
+                for wpc in ((1, 2) if nw == 4 else (1,)):
                     out.append(tp.Tactic(tp.KERNEL_MFMA_PIPE, bc, split, rows, waves, wpc, kc,
                                          depth, kw, nw))
                     if wpc == 1:  # the same with a staggered chunk order

@@ -55,7 +55,11 @@ struct PlanCore {
     X(16, 2, 1, 4, 256, 4, 8) X(16, 1, 1, 8, 256, 4, 8) X(32, 2, 1, 4, 256, 4, 8)           \
     X(256, 8, 4, 1, 32, 6, 8) X(128, 8, 2, 1, 32, 8, 8) X(128, 16, 2, 1, 32, 6, 8)          \
     X(64, 8, 2, 1, 64, 6, 8) X(16, 2, 1, 4, 512, 3, 8) X(16, 2, 1, 4, 512, 2, 8)             \
-    X(16, 1, 1, 8, 512, 4, 8) X(16, 2, 1, 4, 512, 3, 4) X(16, 1, 1, 8, 512, 3, 8)
+    X(16, 1, 1, 8, 512, 4, 8) X(16, 2, 1, 4, 512, 3, 4) X(16, 1, 1, 8, 512, 3, 8)             \
+    X(32, 4, 2, 1, 128, 4, 8) X(32, 4, 1, 2, 128, 4, 8) X(32, 4, 1, 2, 256, 3, 8)             \
+    X(32, 2, 2, 2, 256, 4, 8) X(64, 4, 2, 1, 128, 4, 8) X(64, 4, 2, 2, 128, 4, 8)             \
+    X(64, 4, 4, 1, 128, 4, 8) X(64, 4, 2, 1, 256, 2, 8) X(64, 2, 4, 1, 128, 4, 8)             \
+    X(64, 2, 2, 2, 128, 4, 8) X(128, 4, 2, 1, 64, 4, 8) X(128, 4, 4, 1, 64, 4, 8)
 
 // LDS bytes of an MFMA_XS tactic (x and W chunk tiles, 16 bytes of row pad).
 size_t mfma_xs_lds_bytes(const proj_tactic_t &t);

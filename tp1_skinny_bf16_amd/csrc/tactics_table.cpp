@@ -18,8 +18,10 @@ struct Entry {
 // Measured on MI355X (256 CUs), rotated weight copies, mean of 40 calls
 // back to back per candidate; per bin the fastest over the tuning runs on
 // the current kernels (three full runs, one of them without the staggered
-// candidates, and one more run of the 7168 x 12288 bins up to 16 after the
-// 512-wide chunk instances were added).  Each
+// candidates, one more run of the 7168 x 12288 bins up to 16 after the
+// 512-wide chunk instances were added, and one of the bins 32..128 of the
+// three shapes after the single-pass eight-wave instances with 32- and
+// 64-row groups were added).  Each
 // comment gives the chosen tactic's time and achieved bandwidth (weight + x +
 // y bytes).
 const Entry kTable[] = {
@@ -28,18 +30,18 @@ const Entry kTable[] = {
     {7168, 12288, 4, {PROJ_KERNEL_MFMA_PIPE, 16, 1, 2, 1, 1, 256, 4, 4, 8, 1}},  // 28.88 us, 6105.1 GB/s
     {7168, 12288, 8, {PROJ_KERNEL_MFMA_PIPE, 16, 1, 2, 1, 1, 256, 4, 4, 8, 1}},  // 28.23 us, 6251.2 GB/s
     {7168, 12288, 16, {PROJ_KERNEL_MFMA_PIPE, 16, 1, 2, 1, 1, 256, 4, 4, 8, 1}},  // 29.01 us, 6093.9 GB/s
-    {7168, 12288, 32, {PROJ_KERNEL_MFMA_PIPE, 32, 4, 8, 2, 1, 128, 3, 1, 8, 1}},  // 32.22 us, 5506.1 GB/s
-    {7168, 12288, 64, {PROJ_KERNEL_MFMA_PIPE, 64, 4, 8, 2, 1, 128, 3, 1, 8, 1}},  // 36.2 us, 4935.1 GB/s
-    {7168, 12288, 128, {PROJ_KERNEL_MFMA_PIPE, 128, 4, 8, 2, 1, 64, 4, 1, 8, 0}},  // 46.81 us, 3869.7 GB/s
+    {7168, 12288, 32, {PROJ_KERNEL_MFMA_PIPE, 32, 2, 4, 2, 1, 128, 4, 1, 8, 1}},  // 32.06 us, 5533.6 GB/s
+    {7168, 12288, 64, {PROJ_KERNEL_MFMA_PIPE, 64, 4, 8, 2, 1, 128, 3, 1, 8, 1}},  // 34.98 us, 5107.2 GB/s
+    {7168, 12288, 128, {PROJ_KERNEL_MFMA_PIPE, 128, 4, 8, 2, 1, 64, 4, 1, 8, 0}},  // 45.94 us, 3943.0 GB/s
     {7168, 12288, 256, {PROJ_KERNEL_MFMA_PIPE, 256, 4, 8, 4, 1, 64, 3, 1, 8, 0}},  // 68.96 us, 2699.0 GB/s
     {14560, 7168, 1, {PROJ_KERNEL_MFMA_PIPE, 16, 1, 4, 1, 1, 128, 4, 1, 4, 0}},  // 32.08 us, 6508.0 GB/s
     {14560, 7168, 2, {PROJ_KERNEL_MFMA_PIPE, 16, 1, 4, 1, 1, 128, 4, 1, 4, 0}},  // 32.19 us, 6487.1 GB/s
     {14560, 7168, 4, {PROJ_KERNEL_MFMA_PIPE, 16, 1, 4, 1, 1, 128, 4, 1, 4, 0}},  // 32.25 us, 6477.7 GB/s
     {14560, 7168, 8, {PROJ_KERNEL_MFMA_PIPE, 16, 1, 4, 1, 1, 128, 4, 1, 4, 0}},  // 32.38 us, 6457.1 GB/s
     {14560, 7168, 16, {PROJ_KERNEL_MFMA_PIPE, 16, 1, 4, 1, 1, 128, 4, 1, 4, 0}},  // 32.32 us, 6479.8 GB/s
-    {14560, 7168, 32, {PROJ_KERNEL_MFMA_PIPE, 32, 2, 8, 2, 1, 128, 3, 1, 8, 0}},  // 36.29 us, 5790.1 GB/s
-    {14560, 7168, 64, {PROJ_KERNEL_MFMA_PIPE, 64, 2, 8, 2, 1, 128, 3, 1, 8, 0}},  // 40.83 us, 5180.3 GB/s
-    {14560, 7168, 128, {PROJ_KERNEL_MFMA_PIPE, 128, 4, 16, 2, 1, 64, 3, 1, 8, 0}},  // 51.14 us, 4190.4 GB/s
+    {14560, 7168, 32, {PROJ_KERNEL_MFMA_PIPE, 32, 1, 4, 2, 1, 128, 4, 1, 8, 0}},  // 34.04 us, 6172.8 GB/s
+    {14560, 7168, 64, {PROJ_KERNEL_MFMA_PIPE, 64, 2, 8, 4, 1, 128, 3, 1, 8, 0}},  // 39.62 us, 5338.5 GB/s
+    {14560, 7168, 128, {PROJ_KERNEL_MFMA_PIPE, 128, 4, 16, 2, 1, 64, 3, 1, 8, 1}},  // 50.89 us, 4210.9 GB/s
     {14560, 7168, 256, {PROJ_KERNEL_MFMA_PIPE, 256, 2, 8, 4, 1, 64, 3, 1, 8, 0}},  // 80.54 us, 2729.8 GB/s
     {49376, 7168, 1, {PROJ_KERNEL_MFMA_XS, 16, 1, 8, 1, 2, 128, 1, 0, 0, 0}},  // 101.91 us, 6947.0 GB/s
     {49376, 7168, 2, {PROJ_KERNEL_MFMA_XS, 16, 1, 8, 1, 2, 128, 1, 0, 0, 0}},  // 101.97 us, 6944.0 GB/s

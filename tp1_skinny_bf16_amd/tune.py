@@ -82,14 +82,18 @@ def candidates(bin_: int, full: bool = False):
                  (1, 1, 8, 512, 3, 8)),
             32: ((4, 1, 1, 128, 4, 4), (4, 1, 1, 128, 6, 4), (4, 2, 1, 64, 8, 4),
                  (8, 2, 1, 128, 3, 4), (2, 1, 2, 256, 4, 4), (2, 2, 1, 256, 4, 4),
-                 (8, 2, 1, 128, 3, 8), (2, 1, 4, 256, 4, 8)),
+                 (8, 2, 1, 128, 3, 8), (2, 1, 4, 256, 4, 8), (4, 2, 1, 128, 4, 8),
+                 (4, 1, 2, 128, 4, 8), (4, 1, 2, 256, 3, 8), (2, 2, 2, 256, 4, 8)),
             64: ((4, 2, 1, 64, 8, 4), (4, 2, 1, 128, 4, 4), (4, 4, 1, 64, 8, 4),
                  (8, 2, 1, 64, 4, 4), (8, 2, 1, 64, 6, 4), (16, 2, 1, 64, 3, 8),
                  (8, 2, 1, 128, 3, 8), (16, 1, 1, 64, 3, 8), (8, 4, 1, 128, 3, 8),
-                 (8, 2, 1, 64, 6, 8)),
+                 (8, 2, 1, 64, 6, 8), (4, 2, 1, 128, 4, 8), (4, 2, 2, 128, 4, 8),
+                 (4, 4, 1, 128, 4, 8), (4, 2, 1, 256, 2, 8), (2, 4, 1, 128, 4, 8),
+                 (2, 2, 2, 128, 4, 8)),
             128: ((4, 4, 1, 64, 6, 4), (4, 4, 1, 32, 12, 4), (8, 4, 1, 64, 4, 4),
                   (8, 4, 1, 32, 8, 4), (16, 2, 1, 64, 3, 8), (8, 2, 1, 64, 4, 8),
-                  (16, 4, 1, 32, 4, 8), (8, 2, 1, 32, 8, 8), (16, 2, 1, 32, 6, 8)),
+                  (16, 4, 1, 32, 4, 8), (8, 2, 1, 32, 8, 8), (16, 2, 1, 32, 6, 8),
+                  (4, 2, 1, 64, 4, 8), (4, 4, 1, 64, 4, 8)),
             256: ((4, 4, 1, 32, 7, 4), (4, 4, 1, 64, 3, 4), (8, 4, 1, 32, 6, 4),
                   (8, 4, 1, 64, 3, 4), (16, 4, 1, 32, 4, 8),
                   (8, 4, 1, 64, 3, 8), (8, 8, 1, 64, 3, 8), (8, 4, 1, 32, 6, 8))}[bc]

@@ -139,7 +139,10 @@ typedef struct proj_plan_s proj_plan_t;
  *   out       : receives the plan (set to NULL on failure)
  * The plan owns an FP32 split-K workspace and (with PROJ_PLAN_SPLIT_FUSED)
  * 256 KiB of zeroed arrival counters, allocated with hipMalloc on the
- * current device (none for host-only plans); proj_free releases them.
+ * current device (none for host-only plans); proj_free releases them.  The
+ * first device plan built on a device also allows every kernel of the
+ * library the device's LDS per workgroup (a function attribute, set once),
+ * so no later launch sets one.
  * Returns PROJ_OK, PROJ_EINVAL, PROJ_ENOMEM or PROJ_EHIP.
  */
 int proj_plan(int N, int K, const int *batches, int n_batches, unsigned flags,
@@ -157,6 +160,10 @@ int proj_plan(int N, int K, const int *batches, int n_batches, unsigned flags,
  *   stream : a hipStream_t (NULL = the default stream)
  * One plan supports one stream at a time: runs on different streams that
  * overlap in time share the plan's workspace and race.
+ * proj_run only launches kernels (one, or two with a split-K pass): no
+ * allocation, memset, attribute change or synchronisation, so it may be
+ * recorded by stream capture into a graph, from its first call on; a
+ * replay reads x and W and writes y at the captured addresses.
  * Returns PROJ_OK, PROJ_EINVAL, PROJ_EBATCH, PROJ_EALIGN, PROJ_ENODEV or
  * PROJ_EHIP (launch failure; faults inside a kernel surface at the
  * caller's next synchronisation).

@@ -55,6 +55,36 @@ def _bits(t):
     return t.view(torch.int16).cpu().numpy()
 
 
+def test_graph_capture_without_warmup():
+    """Capture straight away, with no eager call before: building the plan
+    sets every kernel's LDS allowance, so no launch changes a function
+    attribute, and the first launches in the process may be recorded into a
+    graph.  (First in this file, so in a GPU-only run it precedes every
+    other launch of these instances.)"""
+    N, K = 3000, 4096
+    plan = tp.Plan(N, K, [1, 16, 64])
+    W = _weights(1, N, K, 45)[0]
+    g = torch.Generator(device=DEV)
+    g.manual_seed(46)
+    x = torch.randn((64, K), generator=g, device=DEV).to(torch.bfloat16)
+    outs = {B: torch.empty((B, N), dtype=torch.bfloat16, device=DEV) for B in (1, 16, 64)}
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for B, o in outs.items():
+            plan.run(x[:B], W, o)
+    for rep in range(2):
+        for o in outs.values():
+            o.fill_(0.5)
+        graph.replay()
+        torch.cuda.synchronize()
+        for B, o in outs.items():
+            want = _bits(plan.run(x[:B], W))
+            torch.cuda.synchronize()
+            assert np.array_equal(_bits(o), want), f"replay {rep} B={B} ({plan.kernel_name(B)})"
+    say("capture without warm-up: replays equal eager")
+
+
 def test_graph_replay_layer_chain():
     B, L = 64, 2
     pin = tp.Plan(wl.DSA_N, wl.DSA_K, [16, B])

@@ -1241,16 +1241,6 @@ hipError_t launch_stream_inst(const LaunchShape &sh, const proj_tactic_t &t,
     const long g = grid_x(sh, t);
     const size_t lds = (size_t)BC * ksp * 2;
 
-    // Dynamic LDS above 64 KB has to be allowed per kernel; raise the limit
-    // once per instance to the largest size launched so far.
-    static size_t lds_allowed = 64 * 1024;
-    if (lds > lds_allowed) {
-        hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void *>(&stream_kernel<BC, R, P, D2>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-        lds_allowed = lds;
-    }
     StreamArgs a{sh.x, sh.ldx, sh.W, sh.y, sh.ws, fused_counters(sh, g, S), sh.N, sh.K, sh.B,
                  ks, ksp, S};
     hipLaunchKernelGGL((stream_kernel<BC, R, P, D2>), dim3((unsigned)g, S), dim3(nw * 64), lds,
@@ -1267,14 +1257,6 @@ hipError_t launch_mfma_inst(const LaunchShape &sh, const proj_tactic_t &t,
     const int nw = std::min(t.waves, 4);
     const long g = grid_x(sh, t);
     const size_t lds = (size_t)nw * 2 * MT * NT * 256 * sizeof(float);
-    static size_t lds_allowed = 64 * 1024;
-    if (lds > lds_allowed) {
-        hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void *>(&mfma_kernel<MT, NT, P>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-        lds_allowed = lds;
-    }
     MfmaArgs a{sh.x, sh.ldx, sh.W, sh.y, sh.ws, fused_counters(sh, g, S), sh.N, sh.K, sh.B,
                ks, S};
     hipLaunchKernelGGL((mfma_kernel<MT, NT, P>), dim3((unsigned)g, S), dim3(nw * 64), lds,
@@ -1290,14 +1272,6 @@ hipError_t launch_mfma_lds_inst(const LaunchShape &sh, const proj_tactic_t &t,
     const int nw = std::min(t.waves, 4);
     const long g = grid_x(sh, t);
     const size_t lds = mfma_lds_tile_bytes(t);
-    static size_t lds_allowed = 64 * 1024;
-    if (lds > lds_allowed) {
-        hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void *>(&mfma_lds_kernel<MT, NT>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-        lds_allowed = lds;
-    }
     MfmaArgs a{sh.x, sh.ldx, sh.W, sh.y, sh.ws, fused_counters(sh, g, S), sh.N, sh.K, sh.B,
                ks, S};
     hipLaunchKernelGGL((mfma_lds_kernel<MT, NT>), dim3((unsigned)g, S), dim3(nw * 64), lds,
@@ -1320,14 +1294,6 @@ hipError_t launch_mfma_xs_inst(const LaunchShape &sh, const proj_tactic_t &t,
     const int S = slice_count(sh.K, t);
     const long g = grid_x(sh, t);
     const size_t lds = mfma_xs_lds_bytes(t);
-    static size_t lds_allowed = 64 * 1024;
-    if (lds > lds_allowed) {
-        hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void *>(&mfma_xs_kernel<MT, NTB, WM, KC, PD>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-        lds_allowed = lds;
-    }
     MfmaArgs a{sh.x, sh.ldx, sh.W, sh.y, sh.ws, fused_counters(sh, g, S), sh.N, sh.K, sh.B,
                ks, S, t.stagger};
     hipLaunchKernelGGL((mfma_xs_kernel<MT, NTB, WM, KC, PD>), dim3((unsigned)g, S), dim3(256), lds,
@@ -1353,14 +1319,6 @@ hipError_t launch_mfma_pipe_inst(const LaunchShape &sh, const proj_tactic_t &t,
     const int S = slice_count(sh.K, t);
     const long g = grid_x(sh, t);
     const size_t lds = mfma_pipe_lds_bytes(t);
-    static size_t lds_allowed = 64 * 1024;
-    if (lds > lds_allowed) {
-        hipError_t e = hipFuncSetAttribute(
-            reinterpret_cast<const void *>(&mfma_pipe_kernel<MT, NTB, WM, WK, KC, D, NWV>),
-            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-        lds_allowed = lds;
-    }
     MfmaArgs a{sh.x, sh.ldx, sh.W, sh.y, sh.ws, fused_counters(sh, g, S), sh.N, sh.K, sh.B,
                ks, S, t.stagger};
     hipLaunchKernelGGL((mfma_pipe_kernel<MT, NTB, WM, WK, KC, D, NWV>), dim3((unsigned)g, S),
@@ -1465,6 +1423,58 @@ int kernel_name(const LaunchShape &sh, const proj_tactic_t &t, char *buf, size_t
         n = snprintf(buf, len, "mfma_kernel<%d, %d, %d>%s", t.bcap / 16, t.rows,
                      mfma_ring(t.bcap / 16, t.rows), split ? red : "");
     return (n < 0 || (size_t)n >= len) ? -1 : 0;
+}
+
+namespace {
+// The dynamic LDS a kernel may use is what the workgroup has left beside
+// its static __shared__ variables.
+template <typename F>
+hipError_t allow(F *fn, int bytes) {
+    hipFuncAttributes fa;
+    hipError_t e = hipFuncGetAttributes(&fa, reinterpret_cast<const void *>(fn));
+    if (e != hipSuccess) return e;
+    const int dyn = bytes - (int)fa.sharedSizeBytes;
+    if (dyn <= 0) return hipErrorInvalidValue;
+    return hipFuncSetAttribute(reinterpret_cast<const void *>(fn),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, dyn);
+}
+}  // namespace
+
+hipError_t allow_dynamic_lds(size_t bytes) {
+    const int b = (int)bytes;
+    hipError_t e = hipSuccess;
+    auto keep = [&](hipError_t r) {
+        if (e == hipSuccess) e = r;
+    };
+#define TP1_ALLOW_STREAM(BC, R)                                           \
+    keep(allow(&stream_kernel<BC, R, stream_ring(BC, R), false>, b));   \
+    keep(allow(&stream_kernel<BC, R, stream_ring(BC, R), true>, b));
+    TP1_ALLOW_STREAM(1, 1) TP1_ALLOW_STREAM(1, 2) TP1_ALLOW_STREAM(1, 4)
+    TP1_ALLOW_STREAM(2, 1) TP1_ALLOW_STREAM(2, 2) TP1_ALLOW_STREAM(2, 4)
+    TP1_ALLOW_STREAM(4, 1) TP1_ALLOW_STREAM(4, 2) TP1_ALLOW_STREAM(4, 4)
+    TP1_ALLOW_STREAM(8, 1) TP1_ALLOW_STREAM(8, 2) TP1_ALLOW_STREAM(8, 4)
+#undef TP1_ALLOW_STREAM
+#define TP1_ALLOW_MFMA(BC, NT) \
+    keep(allow(&mfma_kernel<BC / 16, NT, mfma_ring(BC / 16, NT)>, b));
+    TP1_ALLOW_MFMA(16, 1) TP1_ALLOW_MFMA(16, 2) TP1_ALLOW_MFMA(16, 4)
+    TP1_ALLOW_MFMA(32, 1) TP1_ALLOW_MFMA(32, 2) TP1_ALLOW_MFMA(32, 4)
+    TP1_ALLOW_MFMA(64, 1) TP1_ALLOW_MFMA(64, 2) TP1_ALLOW_MFMA(64, 4)
+    TP1_ALLOW_MFMA(128, 1) TP1_ALLOW_MFMA(128, 2) TP1_ALLOW_MFMA(128, 4)
+    TP1_ALLOW_MFMA(256, 1)
+#undef TP1_ALLOW_MFMA
+    keep(allow(&mfma_lds_kernel<1, 1>, b));
+    keep(allow(&mfma_lds_kernel<1, 2>, b));
+    keep(allow(&mfma_lds_kernel<2, 1>, b));
+    keep(allow(&mfma_lds_kernel<2, 2>, b));
+#define TP1_ALLOW_XS(BC, NTB, WM, KC, PD) \
+    keep(allow(&mfma_xs_kernel<BC / 16, NTB, WM, KC, PD>, b));
+    TP1_XS_INSTANCES(TP1_ALLOW_XS)
+#undef TP1_ALLOW_XS
+#define TP1_ALLOW_PIPE(BC, NTB, WM, WK, KC, D, NWV) \
+    keep(allow(&mfma_pipe_kernel<BC / 16, NTB, WM, WK, KC, D, NWV>, b));
+    TP1_PIPE_INSTANCES(TP1_ALLOW_PIPE)
+#undef TP1_ALLOW_PIPE
+    return e;
 }
 
 hipError_t launch_read_probe(const void *buf, size_t bytes, float *sink,

@@ -30,6 +30,12 @@ constexpr long kSplitCounters = 65536;
 hipError_t launch_projection(const LaunchShape &s, const proj_tactic_t &t,
                              hipStream_t stream);
 
+// Allow every compiled kernel instance up to `bytes` of dynamic LDS on the
+// current device.  Called once per device when a plan is built, so that
+// launches never change function attributes (they may be recorded into a
+// graph under stream capture, where such calls do not belong).
+hipError_t allow_dynamic_lds(size_t bytes);
+
 // Name of the kernel instance(s) a tactic launches (for profiles).
 int kernel_name(const LaunchShape &sh, const proj_tactic_t &t, char *buf, size_t len);
 

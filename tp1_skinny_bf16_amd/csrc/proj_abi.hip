@@ -9,6 +9,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <mutex>
 #include <new>
 
 #include "../../include/tp1_proj.h"
@@ -59,6 +60,21 @@ int alloc_workspace(proj_plan_s *p, size_t bytes) {
     return rc;
 }
 
+// Every kernel instance may use up to the device's LDS per workgroup; set
+// once per device, before any launch (so no launch sets an attribute).
+int prepare_device(int dev, size_t lds) {
+    static std::mutex mu;
+    static bool done[64] = {};
+    std::lock_guard<std::mutex> lock(mu);
+    if (dev >= 0 && dev < 64 && done[dev]) return PROJ_OK;
+    if (tp1::allow_dynamic_lds(lds) != hipSuccess) {
+        (void)hipGetLastError();
+        return PROJ_EHIP;
+    }
+    if (dev >= 0 && dev < 64) done[dev] = true;
+    return PROJ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -101,6 +117,10 @@ int proj_plan(int N, int K, const int *batches, int n_batches, unsigned flags,
         p->device = dev;
         p->core.num_cus = cus > 0 ? cus : 256;
         if (lds > 0 && (size_t)lds < p->lds_limit) p->lds_limit = (size_t)lds;
+        if (prepare_device(dev, p->lds_limit) != PROJ_OK) {
+            delete p;
+            return PROJ_EHIP;
+        }
     }
     if ((flags & PROJ_PLAN_SPLIT_FUSED) && !(flags & PROJ_PLAN_HOST_ONLY)) {
         // Counters of the fused split-K reduction: zero once here; every

@@ -24,7 +24,8 @@
 //                  chunks ahead.
 //   splitk_reduce  when K is split across workgroups: sums the FP32 slices
 //                  in the fixed order s = 0..S-1 and rounds to BF16 (no
-//                  atomics, so results are bitwise reproducible).
+//                  atomics, so results are bitwise reproducible);
+//                  splitk_reduce4 does the same four outputs per thread.
 //   read_probe     measurement aid: a plain streaming read of a buffer.
 // Every output is rounded once from FP32 to BF16, nearest-even.
 #include "kernels.hpp"

@@ -206,6 +206,9 @@ int proj_plan_set_tactic(proj_plan_t *plan, int bin, const proj_tactic_t *tactic
         return PROJ_EINVAL;
     if (tactic->kernel == PROJ_KERNEL_MFMA_XS && tp1::mfma_xs_lds_bytes(*tactic) > plan->lds_limit)
         return PROJ_EINVAL;
+    if (tactic->kernel == PROJ_KERNEL_MFMA_PIPE &&
+        tp1::mfma_pipe_lds_bytes(*tactic) > plan->lds_limit)
+        return PROJ_EINVAL;
     const int rc = alloc_workspace(plan, tp1::tactic_workspace(plan->core.N, plan->core.K, *tactic));
     if (rc != PROJ_OK) return rc;
     plan->core.tactics[i] = *tactic;

@@ -54,32 +54,34 @@ const Entry kTable[] = {
     {49376, 7168, 256, {PROJ_KERNEL_MFMA_PIPE, 256, 1, 16, 4, 1, 32, 4, 1, 8, 0}},  // 250.83 us, 2937.5 GB/s
     // Per-GPU shards of a G-way tensor-parallel step, G = 2, 4, 8: the input
     // projections column-sharded (N/G x 7168), o_proj row-sharded (7168 x
-    // 12288/G); one tuning run, up to 64 rotated copies per shard.
+    // 12288/G); up to 64 rotated copies per shard.  Per bin the faster of a
+    // full tuning run and a run of bins 32..128 after the single-pass
+    // eight-wave instances were added.
     {1820, 7168, 1, {PROJ_KERNEL_STREAM_DOT2, 1, 1, 2, 4, 4, 0, 0, 0, 0, 0}},  // 8.89 us, 2937.0 GB/s
     {1820, 7168, 2, {PROJ_KERNEL_MFMA_PIPE, 16, 1, 1, 1, 1, 512, 3, 8, 8, 1}},  // 10.06 us, 2597.2 GB/s
     {1820, 7168, 4, {PROJ_KERNEL_MFMA_PIPE, 16, 2, 1, 1, 1, 512, 3, 8, 8, 0}},  // 10.0 us, 2616.3 GB/s
     {1820, 7168, 8, {PROJ_KERNEL_MFMA_PIPE, 16, 2, 1, 1, 1, 256, 4, 8, 8, 1}},  // 10.01 us, 2620.9 GB/s
     {1820, 7168, 16, {PROJ_KERNEL_MFMA_PIPE, 16, 3, 2, 1, 1, 256, 4, 4, 8, 0}},  // 10.48 us, 2517.1 GB/s
     {1820, 7168, 32, {PROJ_KERNEL_MFMA_PIPE, 32, 4, 2, 1, 1, 256, 4, 4, 8, 0}},  // 11.09 us, 2404.6 GB/s
-    {1820, 7168, 64, {PROJ_KERNEL_MFMA_PIPE, 64, 8, 8, 2, 1, 128, 3, 1, 8, 0}},  // 15.21 us, 1791.1 GB/s
-    {1820, 7168, 128, {PROJ_KERNEL_MFMA_PIPE, 128, 8, 8, 2, 1, 64, 4, 1, 8, 0}},  // 21.57 us, 1316.3 GB/s
+    {1820, 7168, 64, {PROJ_KERNEL_MFMA_PIPE, 64, 4, 2, 4, 1, 128, 4, 1, 8, 0}},  // 13.73 us, 1984.1 GB/s
+    {1820, 7168, 128, {PROJ_KERNEL_MFMA_PIPE, 128, 8, 4, 4, 1, 64, 4, 1, 8, 0}},  // 18.01 us, 1576.5 GB/s
     {1820, 7168, 256, {PROJ_KERNEL_MFMA_PIPE, 256, 8, 8, 8, 1, 64, 3, 1, 8, 0}},  // 26.62 us, 1153.0 GB/s
     {3640, 7168, 1, {PROJ_KERNEL_MFMA_PIPE, 16, 1, 1, 1, 1, 512, 4, 8, 8, 0}},  // 10.75 us, 4856.2 GB/s
     {3640, 7168, 2, {PROJ_KERNEL_MFMA_PIPE, 16, 1, 1, 1, 1, 512, 4, 8, 8, 0}},  // 11.04 us, 4730.6 GB/s
     {3640, 7168, 4, {PROJ_KERNEL_MFMA_PIPE, 16, 1, 1, 1, 1, 512, 4, 8, 8, 0}},  // 11.0 us, 4751.8 GB/s
     {3640, 7168, 8, {PROJ_KERNEL_MFMA_PIPE, 16, 1, 1, 1, 1, 512, 4, 8, 8, 0}},  // 11.54 us, 4536.9 GB/s
     {3640, 7168, 16, {PROJ_KERNEL_MFMA_PIPE, 16, 1, 1, 1, 1, 256, 4, 8, 8, 0}},  // 12.31 us, 4267.2 GB/s
-    {3640, 7168, 32, {PROJ_KERNEL_MFMA_PIPE, 32, 2, 2, 1, 1, 256, 4, 4, 8, 0}},  // 15.07 us, 3508.6 GB/s
-    {3640, 7168, 64, {PROJ_KERNEL_MFMA_PIPE, 64, 6, 8, 2, 1, 128, 3, 1, 8, 0}},  // 18.83 us, 2844.7 GB/s
-    {3640, 7168, 128, {PROJ_KERNEL_MFMA_PIPE, 128, 8, 8, 2, 1, 64, 4, 1, 8, 0}},  // 23.75 us, 2313.7 GB/s
+    {3640, 7168, 32, {PROJ_KERNEL_MFMA_PIPE, 32, 4, 4, 2, 1, 128, 4, 1, 8, 0}},  // 14.23 us, 3715.7 GB/s
+    {3640, 7168, 64, {PROJ_KERNEL_MFMA_PIPE, 64, 4, 4, 4, 1, 128, 4, 1, 8, 0}},  // 17.51 us, 3059.2 GB/s
+    {3640, 7168, 128, {PROJ_KERNEL_MFMA_PIPE, 128, 4, 4, 4, 1, 64, 4, 1, 8, 1}},  // 23.2 us, 2368.5 GB/s
     {3640, 7168, 256, {PROJ_KERNEL_MFMA_PIPE, 256, 8, 8, 4, 1, 64, 3, 1, 8, 0}},  // 31.96 us, 1805.9 GB/s
     {6172, 7168, 1, {PROJ_KERNEL_MFMA_PIPE, 16, 1, 2, 1, 1, 256, 4, 4, 8, 0}},  // 15.59 us, 5677.3 GB/s
     {6172, 7168, 2, {PROJ_KERNEL_MFMA_PIPE, 16, 1, 2, 1, 1, 256, 4, 4, 8, 0}},  // 15.67 us, 5650.0 GB/s
     {6172, 7168, 4, {PROJ_KERNEL_MFMA_PIPE, 16, 1, 2, 1, 1, 256, 4, 4, 8, 0}},  // 15.61 us, 5675.1 GB/s
     {6172, 7168, 8, {PROJ_KERNEL_MFMA_PIPE, 16, 1, 2, 1, 1, 256, 4, 4, 8, 0}},  // 15.87 us, 5588.9 GB/s
     {6172, 7168, 16, {PROJ_KERNEL_MFMA_PIPE, 16, 1, 2, 1, 1, 256, 4, 4, 8, 0}},  // 16.85 us, 5276.5 GB/s
-    {6172, 7168, 32, {PROJ_KERNEL_MFMA_PIPE, 32, 4, 8, 2, 1, 128, 3, 1, 8, 0}},  // 20.21 us, 4420.4 GB/s
-    {6172, 7168, 64, {PROJ_KERNEL_MFMA_PIPE, 64, 4, 8, 2, 1, 128, 3, 1, 8, 0}},  // 23.41 us, 3852.6 GB/s
+    {6172, 7168, 32, {PROJ_KERNEL_MFMA_PIPE, 32, 2, 4, 2, 1, 128, 4, 1, 8, 0}},  // 19.37 us, 4612.1 GB/s
+    {6172, 7168, 64, {PROJ_KERNEL_MFMA_PIPE, 64, 4, 8, 2, 1, 128, 3, 1, 8, 0}},  // 23.35 us, 3862.5 GB/s
     {6172, 7168, 128, {PROJ_KERNEL_MFMA_PIPE, 128, 4, 8, 2, 1, 64, 4, 1, 8, 1}},  // 31.23 us, 2942.6 GB/s
     {6172, 7168, 256, {PROJ_KERNEL_MFMA_PIPE, 256, 4, 8, 4, 1, 64, 3, 1, 8, 0}},  // 44.3 us, 2151.5 GB/s
     {7168, 1536, 1, {PROJ_KERNEL_MFMA_PIPE, 16, 1, 2, 1, 1, 256, 4, 4, 8, 0}},  // 6.24 us, 3531.7 GB/s
@@ -88,8 +90,8 @@ const Entry kTable[] = {
     {7168, 1536, 8, {PROJ_KERNEL_MFMA_PIPE, 16, 1, 2, 1, 1, 256, 4, 4, 8, 0}},  // 6.52 us, 3398.7 GB/s
     {7168, 1536, 16, {PROJ_KERNEL_MFMA_PIPE, 16, 1, 2, 1, 1, 256, 4, 4, 8, 0}},  // 6.66 us, 3348.1 GB/s
     {7168, 1536, 32, {PROJ_KERNEL_MFMA_PIPE, 32, 1, 2, 1, 1, 256, 4, 4, 8, 1}},  // 7.89 us, 2861.5 GB/s
-    {7168, 1536, 64, {PROJ_KERNEL_MFMA_PIPE, 64, 2, 4, 2, 1, 128, 4, 1, 4, 0}},  // 13.33 us, 1735.5 GB/s
-    {7168, 1536, 128, {PROJ_KERNEL_MFMA_XS, 128, 1, 4, 4, 1, 128, 1, 0, 0, 1}},  // 18.64 us, 1300.9 GB/s
+    {7168, 1536, 64, {PROJ_KERNEL_MFMA_PIPE, 64, 1, 2, 4, 1, 128, 4, 1, 8, 0}},  // 9.37 us, 2469.0 GB/s
+    {7168, 1536, 128, {PROJ_KERNEL_MFMA_PIPE, 128, 2, 4, 4, 1, 64, 4, 1, 8, 0}},  // 15.36 us, 1578.7 GB/s
     {7168, 1536, 256, {PROJ_KERNEL_MFMA_XS, 256, 1, 2, 4, 1, 128, 1, 0, 0, 1}},  // 23.79 us, 1112.9 GB/s
     {7168, 3072, 1, {PROJ_KERNEL_MFMA_PIPE, 16, 1, 2, 1, 1, 256, 4, 4, 8, 0}},  // 9.23 us, 4773.6 GB/s
     {7168, 3072, 2, {PROJ_KERNEL_MFMA_PIPE, 16, 1, 2, 1, 1, 256, 4, 4, 8, 0}},  // 9.28 us, 4750.1 GB/s
@@ -97,25 +99,25 @@ const Entry kTable[] = {
     {7168, 3072, 8, {PROJ_KERNEL_MFMA_PIPE, 16, 1, 2, 1, 1, 256, 4, 4, 8, 0}},  // 9.32 us, 4742.9 GB/s
     {7168, 3072, 16, {PROJ_KERNEL_MFMA_PIPE, 16, 1, 2, 1, 1, 256, 4, 4, 8, 0}},  // 9.83 us, 4513.5 GB/s
     {7168, 3072, 32, {PROJ_KERNEL_MFMA_PIPE, 32, 1, 2, 1, 1, 256, 4, 4, 8, 0}},  // 11.69 us, 3823.4 GB/s
-    {7168, 3072, 64, {PROJ_KERNEL_MFMA_PIPE, 64, 3, 8, 2, 1, 128, 3, 1, 8, 0}},  // 16.66 us, 2722.1 GB/s
-    {7168, 3072, 128, {PROJ_KERNEL_MFMA_PIPE, 128, 4, 8, 2, 1, 64, 4, 1, 8, 0}},  // 23.55 us, 1981.4 GB/s
+    {7168, 3072, 64, {PROJ_KERNEL_MFMA_PIPE, 64, 1, 2, 2, 1, 128, 4, 2, 8, 0}},  // 14.92 us, 3039.6 GB/s
+    {7168, 3072, 128, {PROJ_KERNEL_MFMA_PIPE, 128, 2, 4, 4, 1, 64, 4, 1, 8, 1}},  // 20.94 us, 2228.3 GB/s
     {7168, 3072, 256, {PROJ_KERNEL_MFMA_PIPE, 256, 4, 8, 8, 1, 64, 3, 1, 8, 0}},  // 30.39 us, 1621.7 GB/s
     {7168, 6144, 1, {PROJ_KERNEL_MFMA_PIPE, 16, 1, 2, 1, 1, 512, 3, 4, 8, 1}},  // 16.06 us, 5486.1 GB/s
     {7168, 6144, 2, {PROJ_KERNEL_MFMA_PIPE, 16, 1, 2, 1, 1, 256, 4, 4, 8, 1}},  // 15.86 us, 5557.0 GB/s
     {7168, 6144, 4, {PROJ_KERNEL_MFMA_PIPE, 16, 1, 2, 1, 1, 256, 4, 4, 8, 1}},  // 15.86 us, 5560.3 GB/s
     {7168, 6144, 8, {PROJ_KERNEL_MFMA_PIPE, 16, 1, 2, 1, 1, 256, 4, 4, 8, 1}},  // 15.79 us, 5591.7 GB/s
     {7168, 6144, 16, {PROJ_KERNEL_MFMA_PIPE, 16, 1, 2, 1, 1, 256, 4, 4, 8, 1}},  // 16.56 us, 5344.6 GB/s
-    {7168, 6144, 32, {PROJ_KERNEL_MFMA_PIPE, 32, 1, 2, 1, 1, 256, 4, 4, 8, 1}},  // 20.0 us, 4446.6 GB/s
-    {7168, 6144, 64, {PROJ_KERNEL_MFMA_PIPE, 64, 4, 8, 4, 1, 128, 3, 1, 8, 0}},  // 23.65 us, 3796.4 GB/s
-    {7168, 6144, 128, {PROJ_KERNEL_MFMA_PIPE, 128, 4, 8, 2, 1, 64, 4, 1, 8, 1}},  // 30.82 us, 2968.5 GB/s
+    {7168, 6144, 32, {PROJ_KERNEL_MFMA_PIPE, 32, 2, 4, 2, 1, 128, 4, 1, 8, 1}},  // 19.06 us, 4665.9 GB/s
+    {7168, 6144, 64, {PROJ_KERNEL_MFMA_PIPE, 64, 4, 8, 2, 1, 128, 3, 1, 8, 0}},  // 22.76 us, 3944.8 GB/s
+    {7168, 6144, 128, {PROJ_KERNEL_MFMA_PIPE, 128, 4, 8, 2, 1, 64, 4, 1, 8, 0}},  // 30.22 us, 3027.4 GB/s
     {7168, 6144, 256, {PROJ_KERNEL_MFMA_PIPE, 256, 4, 8, 8, 1, 64, 3, 1, 8, 0}},  // 41.26 us, 2300.0 GB/s
     {7280, 7168, 1, {PROJ_KERNEL_MFMA_PIPE, 16, 1, 2, 1, 1, 256, 4, 4, 8, 0}},  // 18.1 us, 5767.7 GB/s
     {7280, 7168, 2, {PROJ_KERNEL_MFMA_PIPE, 16, 1, 2, 1, 1, 256, 4, 4, 8, 1}},  // 17.75 us, 5883.0 GB/s
     {7280, 7168, 4, {PROJ_KERNEL_MFMA_PIPE, 16, 1, 2, 1, 1, 256, 4, 4, 8, 1}},  // 17.8 us, 5869.8 GB/s
     {7280, 7168, 8, {PROJ_KERNEL_MFMA_PIPE, 16, 1, 2, 1, 1, 256, 4, 4, 8, 0}},  // 17.82 us, 5869.7 GB/s
     {7280, 7168, 16, {PROJ_KERNEL_MFMA_PIPE, 16, 1, 2, 1, 1, 256, 4, 4, 8, 0}},  // 18.4 us, 5697.2 GB/s
-    {7280, 7168, 32, {PROJ_KERNEL_MFMA_PIPE, 32, 1, 2, 1, 1, 256, 4, 4, 8, 0}},  // 22.17 us, 4749.2 GB/s
-    {7280, 7168, 64, {PROJ_KERNEL_MFMA_PIPE, 64, 4, 8, 2, 1, 128, 3, 1, 8, 0}},  // 25.27 us, 4203.2 GB/s
+    {7280, 7168, 32, {PROJ_KERNEL_MFMA_PIPE, 32, 2, 4, 2, 1, 128, 4, 1, 8, 0}},  // 21.39 us, 4922.4 GB/s
+    {7280, 7168, 64, {PROJ_KERNEL_MFMA_PIPE, 64, 4, 8, 2, 1, 128, 3, 1, 8, 0}},  // 25.21 us, 4213.2 GB/s
     {7280, 7168, 128, {PROJ_KERNEL_MFMA_PIPE, 128, 4, 8, 2, 1, 64, 4, 1, 8, 1}},  // 31.73 us, 3405.8 GB/s
     {7280, 7168, 256, {PROJ_KERNEL_MFMA_PIPE, 256, 4, 8, 4, 1, 64, 3, 1, 8, 0}},  // 45.88 us, 2436.0 GB/s
     {12344, 7168, 1, {PROJ_KERNEL_MFMA_PIPE, 16, 1, 4, 1, 1, 256, 3, 2, 8, 0}},  // 28.24 us, 6267.8 GB/s
@@ -123,8 +125,8 @@ const Entry kTable[] = {
     {12344, 7168, 4, {PROJ_KERNEL_MFMA_PIPE, 16, 1, 4, 1, 1, 256, 3, 2, 8, 0}},  // 28.06 us, 6312.2 GB/s
     {12344, 7168, 8, {PROJ_KERNEL_MFMA_PIPE, 16, 1, 4, 1, 1, 256, 3, 2, 8, 0}},  // 28.39 us, 6244.3 GB/s
     {12344, 7168, 16, {PROJ_KERNEL_MFMA_PIPE, 16, 1, 4, 1, 1, 256, 3, 2, 8, 0}},  // 28.53 us, 6224.6 GB/s
-    {12344, 7168, 32, {PROJ_KERNEL_MFMA_PIPE, 32, 2, 8, 2, 1, 128, 3, 1, 8, 0}},  // 31.85 us, 5595.4 GB/s
-    {12344, 7168, 64, {PROJ_KERNEL_MFMA_PIPE, 64, 2, 8, 2, 1, 128, 3, 1, 8, 0}},  // 36.59 us, 4904.6 GB/s
+    {12344, 7168, 32, {PROJ_KERNEL_MFMA_PIPE, 32, 1, 4, 2, 1, 128, 4, 1, 8, 0}},  // 30.52 us, 5839.2 GB/s
+    {12344, 7168, 64, {PROJ_KERNEL_MFMA_PIPE, 64, 2, 8, 2, 1, 128, 3, 1, 8, 1}},  // 35.76 us, 5018.5 GB/s
     {12344, 7168, 128, {PROJ_KERNEL_MFMA_PIPE, 128, 4, 16, 2, 1, 64, 3, 1, 8, 1}},  // 48.05 us, 3786.9 GB/s
     {12344, 7168, 256, {PROJ_KERNEL_MFMA_PIPE, 256, 2, 8, 4, 1, 64, 3, 1, 8, 0}},  // 75.26 us, 2484.1 GB/s
     {24688, 7168, 1, {PROJ_KERNEL_MFMA_PIPE, 16, 1, 4, 1, 2, 128, 3, 1, 4, 0}},  // 53.25 us, 6647.7 GB/s

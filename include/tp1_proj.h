@@ -176,8 +176,9 @@ int proj_run(const proj_plan_t *plan, int B, const void *x, long ldx,
  *     y_in[l] = x_l . W_in[l]^T                    (plan `in`,  N_in x K_in)
  *     y_o[l]  = y_in[l][:, 0:K_o] . W_o[l]^T       (plan `out`, N_o x K_o)
  *     x_{l+1} = y_o[l]
- * back to back on one stream, each layer with its own weights, as the
- * dep page's DepAttention chains its input projection into o_proj (section
+ * back to back on one stream, each layer with its own weights, as
+ * DepAttention chains its input projection into o_proj on the vLLM API page
+ * "vllm.models.kimi_k3.nvidia.specialized_decode.runtime.dep" (section
  * "DepAttention"; here the attention core between them is replaced by a
  * fixed gather of the first K_o columns, read in place through the row
  * stride N_in, without a copy).

@@ -1,8 +1,10 @@
 """Graph capture of the projection path.
 
-A decode step can replay its layer loop as a captured graph (the runtime
-page's capture-size buckets, which it records as CUDA graphs; here HIP graphs
-through torch.cuda.CUDAGraph).  proj_run and proj_run_layers only enqueue
+A decode step can replay its layer loop as a captured graph: the vLLM API
+page "vllm.models.kimi_k3.nvidia.specialized_decode.runtime", section
+"specialized_decode_config", configures the decode runtime with the
+engine's graph capture sizes.  Here the graphs are HIP graphs recorded
+through torch.cuda.CUDAGraph.  proj_run and proj_run_layers only enqueue
 kernels on the stream they are given: no memset, no allocation and no
 synchronisation, so both can be captured.  Every tactic is deterministic, so
 each replay must equal the eager result bit for bit.  Replays read their

@@ -285,7 +285,8 @@ def test_fused_split_matches_two_pass_bitwise():
             check_random(f"fused split {tactic_label(fused, B)} B={B}", a1, x[:B], W)
 
 
-# Per-GPU shards of a G-way tensor-parallel step (the hybrid page, section
+# Per-GPU shards of a G-way tensor-parallel step (the vLLM API page
+# "vllm.models.kimi_k3.nvidia.specialized_decode.runtime.hybrid", section
 # "HybridAttention"): the input projections column-sharded (N/G x K), o_proj
 # row-sharded (N x K/G), G = 2, 4, 8.  Each shape has its own measured table.
 TP_SHARDS = [(wl.DSA_N // g, wl.DSA_K) for g in (2, 4, 8)] + \

@@ -2,7 +2,8 @@
 
 Each layer runs its input projection, then o_proj on the first K_o columns of
 that output (read in place through the row stride), feeding the next layer,
-as the dep page's DepAttention chains the two projections (section
+as DepAttention chains the two projections on the vLLM API page
+"vllm.models.kimi_k3.nvidia.specialized_decode.runtime.dep" (section
 "DepAttention"; the attention core between them is outside this library).
 The chain is enqueued by one native call.
 """

@@ -1,9 +1,10 @@
 """Tactic measurement: time candidate tactics per (N, K, batch bin) on the GPU
 and pick the table the library ships (tactics_table.cpp).
 
-The vLLM dep page keeps per-batch tactic tables for its projections (its
-opening text names DEP_PROJECTION and DEP_OPROJ; section "_bins" gives the
-lookup rule); this tool builds the MI355X one by measurement.  Each candidate
+The vLLM API page "vllm.models.kimi_k3.nvidia.specialized_decode.runtime.dep"
+keeps per-batch tactic tables for its projections (its opening text names
+DEP_PROJECTION and DEP_OPROJ; section "_bins" gives the lookup rule); this
+tool builds the MI355X one by measurement.  Each candidate
 is timed over rotated weight copies (>= 1 GB, so every call streams its
 weight from HBM).  The time ranked is the mean per call of `reps` calls
 enqueued back to back (how a decode step issues its projections, and where a

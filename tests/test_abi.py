@@ -87,7 +87,12 @@ def test_bins_follow_the_smallest_key_at_or_above():
         assert e.value.code == tp.PROJ_EBATCH
 
 
-@pytest.mark.parametrize("N,K", SHAPES + [(1000, 1032), (777, 2056), (33, 8), (5, 12288)])
+TP_SHARDS = [(14560 // g, 7168) for g in (2, 4, 8)] + [(7168, 12288 // g) for g in (2, 4, 8)] + \
+            [(49376 // g, 7168) for g in (2, 4, 8)]
+
+
+@pytest.mark.parametrize("N,K", SHAPES + TP_SHARDS +
+                         [(1000, 1032), (777, 2056), (33, 8), (5, 12288)])
 def test_every_planned_bin_gets_a_valid_tactic(N, K):
     p = tp.Plan(N, K, ALL_B, host_only=True)
     for b in range(1, 257):

@@ -38,8 +38,8 @@ def _weights(n, N, K, seed):
 
 
 def _capture(fn):
-    """Warm up fn on a side stream (first launches set kernel attributes),
-    then capture it into a graph."""
+    """Run fn once eagerly on a side stream (the usual pattern before a
+    capture), then capture it into a graph."""
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(s):

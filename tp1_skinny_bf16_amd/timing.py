@@ -79,5 +79,38 @@ def time_calls(calls, warmup: int = 5, reps: int = 50, warm_seconds: float = 0.2
     }
 
 
+def time_graph(calls, replays: int = 5):
+    """Mean GPU time per call of `calls` (zero-argument callables that launch
+    on torch's current stream) captured in order into one graph and
+    replayed: the host's launch submission, ~6-10 us per call through the
+    binding, is then off the critical path, which matters for kernels of
+    about that length.  Returns microseconds per call."""
+    cur = torch.cuda.current_stream()
+    side = torch.cuda.Stream()
+    side.wait_stream(cur)
+    with torch.cuda.stream(side):
+        for c in calls:
+            c()
+    cur.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for c in calls:
+            c()
+    for _ in range(2):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(cur)
+    for _ in range(replays):
+        graph.replay()
+    t1.record(cur)
+    torch.cuda.synchronize()
+    us = t0.elapsed_time(t1) * 1e3 / (replays * len(calls))
+    del graph
+    return us
+
+
 def gbs(nbytes: float, us: float) -> float:
     return nbytes / (us * 1e-6) / 1e9

@@ -9,9 +9,12 @@ is timed over rotated weight copies (>= 1 GB, so every call streams its
 weight from HBM).  The time ranked is the mean per call of `reps` calls
 enqueued back to back (how a decode step issues its projections, and where a
 split-K call pays its second launch in full); the median of per-call event
-timings is kept beside it.  Ties within 1% go to fewer launches (no split-K
-pass), then the smaller split, then fewer rows per wave.  The crossover is
-the smallest batch whose best tactic is an MFMA one.
+timings is kept beside it.  With --graph the same `reps` calls are captured
+in one graph and replayed, so that the host's launch submission (~6 us per
+call through the binding) does not bound kernels that short; the small
+tensor-parallel shards are tuned that way.  Ties within 1% go to fewer
+launches (no split-K pass), then the smaller split, then fewer rows per wave.
+The crossover is the smallest batch whose best tactic is an MFMA one.
 
     python -m tp1_skinny_bf16_amd.tune --shape 14560x7168 --bins 1,2,4 --out t.json
 """
@@ -27,7 +30,7 @@ import torch
 
 from . import (KERNEL_IDS, KERNEL_MFMA, KERNEL_MFMA_LDS, KERNEL_MFMA_PIPE, KERNEL_MFMA_XS,
                KERNEL_STREAM, KERNEL_STREAM_DOT2, Plan, ProjError, Tactic)
-from .timing import gbs, rotation_copies, time_calls
+from .timing import gbs, rotation_copies, time_calls, time_graph
 
 SHAPES = {"dsa": (14560, 7168), "oproj": (7168, 12288), "kda": (49376, 7168)}
 
@@ -115,7 +118,7 @@ def _key(res):
 
 
 def measure(N: int, K: int, bins, reps: int = 40, log=None, full: bool = False,
-            fused_split: bool = False):
+            fused_split: bool = False, graph: bool = False):
     dev = torch.device("cuda:0")
     g = torch.Generator(device=dev)
     g.manual_seed(7)
@@ -124,7 +127,8 @@ def measure(N: int, K: int, bins, reps: int = 40, log=None, full: bool = False,
     bmax = max(bins)
     x = torch.randn((bmax, K), generator=g, device=dev).to(torch.bfloat16)
     plan = Plan(N, K, bins, fused_split=fused_split)
-    result = {"N": N, "K": K, "copies": len(copies), "bins": {}, "fused_split": fused_split}
+    result = {"N": N, "K": K, "copies": len(copies), "bins": {}, "fused_split": fused_split,
+              "graph": graph}
     # half a second of the default tactic first: the first timings of a cold
     # process otherwise run at ramping clocks
     y0 = torch.empty((bins[0], N), dtype=torch.bfloat16, device=dev)
@@ -143,6 +147,16 @@ def measure(N: int, K: int, bins, reps: int = 40, log=None, full: bool = False,
             try:
                 plan.set_tactic(b, t)
             except ProjError:
+                continue
+            if graph:
+                # `reps` calls round-robin over the copies, captured in one
+                # graph; each call launches on the current (capture) stream
+                gcalls = [(lambda W=copies[i % len(copies)]: plan.run_ptr(
+                    b, xb.data_ptr(), K, W.data_ptr(), y.data_ptr(),
+                    torch.cuda.current_stream().cuda_stream)) for i in range(reps)]
+                us = time_graph(gcalls)
+                rows.append({"tactic": t.as_dict(), "us": round(us, 2), "us_call": None,
+                             "kernel": plan.kernel_name(b)})
                 continue
             calls = [(lambda W=W: plan.run_ptr(b, xb.data_ptr(), K, W.data_ptr(),
                                                y.data_ptr(), st)) for W in copies]
@@ -275,6 +289,9 @@ def main():
     ap.add_argument("--full", action="store_true")
     ap.add_argument("--fused-split", action="store_true",
                     help="measure with the in-kernel split-K reduction")
+    ap.add_argument("--graph", action="store_true",
+                    help="time each candidate's calls captured in one graph (for kernels "
+                         "as short as the host's launch submission)")
     ap.add_argument("--out", required=True)
     a = ap.parse_args()
     bins = [int(v) for v in a.bins.split(",")]
@@ -283,7 +300,7 @@ def main():
     for sh in a.shape:
         N, K = SHAPES[sh] if sh in SHAPES else (int(v) for v in sh.split("x"))
         res = measure(N, K, bins, a.reps, log=lambda m: print(m, flush=True), full=a.full,
-                      fused_split=a.fused_split)
+                      fused_split=a.fused_split, graph=a.graph)
         allres.append(res)
         print(table_rows(res), flush=True)
         print(f"crossover (first MFMA bin) for {N}x{K}: {res['crossover']}  "

@@ -142,14 +142,32 @@ __device__ __forceinline__ void splitk_fixup(const float *ws, uint16_t *y, int *
     if (!last) return;
     const int S = gridDim.y;
     const size_t slice = (size_t)B * N;
-    for (int i = threadIdx.x; i < rows * B; i += blockDim.x) {
-        const int b = i / rows, r = i - (i / rows) * rows;
-        const size_t o = (size_t)b * N + row0 + r;
-        float acc = __hip_atomic_load(ws + o, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        for (int k = 1; k < S; ++k)
-            acc += __hip_atomic_load(ws + k * slice + o, __ATOMIC_RELAXED,
-                                     __HIP_MEMORY_SCOPE_AGENT);
-        y[o] = to_bf16(acc);
+    const int total = rows * B;
+    // U outputs per thread per round, all loads of a slice issued before any
+    // is added, so a round costs one memory round trip per slice.
+    constexpr int U = 8;
+    for (int base = threadIdx.x; base < total; base += (int)blockDim.x * U) {
+        size_t o[U];
+        float acc[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i = min(base + u * (int)blockDim.x, total - 1);
+            const int b = i / rows, r = i - (i / rows) * rows;
+            o[u] = (size_t)b * N + row0 + r;
+            acc[u] = __hip_atomic_load(ws + o[u], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        for (int k = 1; k < S; ++k) {
+            float v[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                v[u] = __hip_atomic_load(ws + k * slice + o[u], __ATOMIC_RELAXED,
+                                         __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+            for (int u = 0; u < U; ++u) acc[u] += v[u];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if (base + u * (int)blockDim.x < total) y[o[u]] = to_bf16(acc[u]);
     }
     if (threadIdx.x == 0)
         __hip_atomic_store(cnt + blockIdx.x, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

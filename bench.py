@@ -7,6 +7,9 @@ total, so no call finds its weight in the 256 MB MALL).  Inputs are resident
 in HBM before timing starts.  Prints ONE JSON line:
   value        = algorithmic HBM bytes of a step / step time, GB/s
   roofline     = the dominant kernel's achieved GB/s against the 8 TB/s peak
+  read_ceiling = a plain streaming read of the same weight copies, one launch
+                 per copy, and of a 2 GB buffer, measured after the timed
+                 region; the dominant kernel as a fraction of the former
   cpu_baseline = the CPU oracle timed on a bounded sample of the same step
 
 `--report PATH` also times every point of every configuration (DSA B=1, the
@@ -143,9 +146,27 @@ def headline(args, torch, tp, wl, timing):
             "frac": round(achieved / timing.HBM_PEAK_GBS, 4),
             "traffic": measured_traffic(name),
             "avg_launch_us": round(avg_us, 2), "bytes_per_launch": int(bytes_per_launch)}
+    # Read ceilings of the box, after the timed region: the library's
+    # streaming-read probe (a plain 128-bit read-and-reduce, 4 waves per CU)
+    # over the same rotated weight copies back to back, one launch per copy
+    # (what a single-pass projection of this weight can reach per launch),
+    # and over one 2 GB buffer (the sustained rate).
+    sink = torch.empty(65536, dtype=torch.float32, device=dev)
+    wbytes = cfg.N * cfg.K * 2
+    rl = timing.time_calls([(lambda W=W: tp.read_probe(W, sink, 4)) for W in copies],
+                           warmup=2, reps=4 * ncopy, warm_seconds=0.05)
+    big = torch.ones(1024 ** 3, dtype=torch.bfloat16, device=dev)
+    rs = timing.time_calls([lambda: tp.read_probe(big, sink, 4)], warmup=2, reps=10,
+                           warm_seconds=0.05)
+    per_launch = timing.gbs(wbytes, rl["us_mean_b2b"])
+    ceiling = {"per_launch_GBps": round(per_launch, 1),
+               "per_launch_us": round(rl["us_mean_b2b"], 2),
+               "sustained_GBps": round(timing.gbs(big.numel() * 2, rs["us_median"]), 1),
+               "dominant_kernel_frac_of_per_launch": round(achieved / per_launch, 4)}
+    del big
     res = {"cfg": cfg, "t": t, "plan": plan, "value": value, "ms": ms_per_step,
            "per_b": per_b, "roofline": roof, "step_bytes": step_bytes,
-           "copies": ncopy}
+           "copies": ncopy, "read_ceiling": ceiling}
     return res
 
 
@@ -341,6 +362,7 @@ def main():
         "per_batch_GBps": {str(B): r["GBps"] for B, r in h["per_b"].items()},
         "kernels": {str(B): r["kernel"] for B, r in h["per_b"].items()},
         "roofline": h["roofline"],
+        "read_ceiling": h["read_ceiling"],
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

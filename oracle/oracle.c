@@ -28,7 +28,9 @@
  *   one-hot weights at full shapes (bitwise), closed-form constant inputs,
  *   hand-derived round-to-nearest-even ties (tests/golden), scaling /
  *   negation / permutation / linearity invariants, and numpy float64
- *   products rounded by an independent bit-level rounder.
+ *   products rounded by an independent bit-level rounder.  The unrounded
+ *   sums S are pinned on their own against exact rational sums (within the
+ *   double-accumulation error bound) and against numpy float64 products.
  *
  * Build: gcc -O2 -fno-fast-math -shared -fPIC -pthread (oracle/build.py).
  * Defining ORACLE_MUTANT=<n> plants one deliberate mistake (used only by the
@@ -132,8 +134,13 @@ static void *worker(void *arg)
             s += xr[k] * bf16_to_double(wr[k]);
 #endif
         j->y[(long)b * j->ldy + n] = double_to_bf16(s);
+#if ORACLE_MUTANT == 8
+        if (j->S)                            /* planted: S stored transposed */
+            j->S[(long)n * j->B + b] = s;
+#else
         if (j->S)
             j->S[(long)b * j->lds + n] = s;
+#endif
     }
     return NULL;
 }

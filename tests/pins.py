@@ -12,7 +12,12 @@ What pins what:
   one_hot           identity / one-hot weights at full shapes: row/column indexing
   invariants        power-of-two scaling, negation, permutations, linearity
   numpy_f64         numpy float64 products + an independent bit-level rounder
-  rounding          the rounding step alone against exact rational rounding
+  rounding          the rounding step alone against exact rational rounding,
+                    plus the non-finite cases against binary32's encodings
+  unrounded_sum     the unrounded double sums S (the reference value of the
+                    GPU tests' aggregate gate) against exact rational sums,
+                    within the error bound of K-term double accumulation, and
+                    against numpy float64 products
 """
 from __future__ import annotations
 
@@ -230,7 +235,70 @@ def rounding(proj, rounder):
         if val == 0 and np.signbit(val):
             want = 0x8000                      # a zero keeps its sign
         assert int(g) == want, f"rounding {val!r}: {int(g):#06x} != {want:#06x}"
+    # Non-finite sums have no exact value: any NaN maps to the canonical
+    # quiet NaN (sign dropped) and an infinity keeps its sign.  The expected
+    # patterns are the upper halves of binary32's own encodings of NaN and of
+    # +-inf (BF16 is the top half of binary32).
+    special = np.array([np.nan, -np.nan, np.inf, -np.inf], dtype=np.float64)
+    f32 = special.astype(np.float32).view(np.uint32) >> np.uint32(16)
+    want = [int(f32[0]) & 0x7FFF, int(f32[1]) & 0x7FFF, int(f32[2]), int(f32[3])]
+    got = [int(g) for g in np.asarray(rounder(special))]
+    assert want[0] == 0x7FC0 and want[2] == 0x7F80 and want[3] == 0xFF80, want
+    assert got == want, f"non-finite rounding: {[hex(g) for g in got]}"
+
+
+def _sum_bound(xb, wb):
+    """Error bound of a K-term double sum, as exact rationals per (b, n):
+    gamma_(K-1) * sum_k |x[b,k] W[n,k]|, gamma_m = m u / (1 - m u), u = 2^-53
+    (each BF16 x BF16 product is exact in double; only the K-1 additions
+    round)."""
+    K = xb.shape[1]
+    u = Fraction(1, 2 ** 53)
+    m = max(K - 1, 0)
+    gamma = m * u / (1 - m * u)
+    xs = [[abs(exact.bf16_to_fraction(int(v))) for v in row] for row in xb]
+    ws = [[abs(exact.bf16_to_fraction(int(v))) for v in row] for row in wb]
+    return [[gamma * sum((a * b for a, b in zip(xr, wr)), Fraction(0)) for wr in ws]
+            for xr in xs]
+
+
+def unrounded_sum(proj, rounder=None, proj_sum=None):
+    assert proj_sum is not None, "this pin needs the oracle's sum output"
+    rng = _rng(4321)
+    # B != N everywhere, so a transposed or mis-strided store cannot land on
+    # the right element by symmetry.
+    cases = [(_random_bf16(rng, (2, 17), 1.0), _random_bf16(rng, (3, 17), 0.02)),
+             (_random_bf16(rng, (3, 64), 1.0), _random_bf16(rng, (8, 64), 0.02)),
+             (_random_bf16(rng, (1, 40), 1.0), _random_bf16(rng, (5, 40), 1.0)),
+             (_wide_bf16(rng, (4, 33)), _wide_bf16(rng, (7, 33)))]
+    for xb, wb in cases:
+        _, S = proj_sum(xb, wb)
+        S = np.asarray(S)
+        assert S.shape == (xb.shape[0], wb.shape[0]), S.shape
+        E = exact.exact_sums(xb, wb)
+        bound = _sum_bound(xb, wb)
+        for b in range(S.shape[0]):
+            for n in range(S.shape[1]):
+                err = abs(Fraction(float(S[b, n])) - E[b][n])
+                assert err <= bound[b][n], (
+                    f"S[{b},{n}] = {S[b, n]!r} is {float(err):.3g} from the exact sum "
+                    f"{float(E[b][n])!r} (bound {float(bound[b][n]):.3g})")
+    # A second, independent float64 sum: numpy's matrix product.  Both are
+    # double sums of the same exact products, each within gamma_(K-1) of the
+    # exact value, so they agree to 2 gamma_(K-1) |x| |W|^T < 1e-12 of it.
+    rng = _rng(6)
+    B, N, K = 4, 512, 1024
+    xb = _random_bf16(rng, (B, K), 1.0)
+    wb = _random_bf16(rng, (N, K), 0.02)
+    xd, wd = _bf16_to_f64(xb), _bf16_to_f64(wb)
+    S_np = xd @ wd.T
+    scale = np.abs(xd) @ np.abs(wd).T
+    _, S = proj_sum(xb, wb)
+    S = np.asarray(S)
+    assert S.shape == (B, N)
+    bad = np.argwhere(np.abs(S - S_np) > 1e-12 * scale)
+    assert bad.size == 0, f"S differs from numpy float64 at {len(bad)} elements, first {bad[0]}"
 
 
 ALL_PINS = (exact_bruteforce, golden_ties, closed_forms, one_hot, invariants,
-            numpy_f64, rounding)
+            numpy_f64, rounding, unrounded_sum)

@@ -3,6 +3,8 @@
 Exact-sum inputs (every FP32 partial sum exact) and closed forms must match
 bit for bit whatever the kernel's summation order; random seeded inputs of
 the configurations' shapes and distributions must pass the G1/G2/D1 gates.
+Every output of every full-shape case is compared: the oracle computes all
+B x N elements, no column sample.
 """
 import numpy as np
 import pytest
@@ -11,8 +13,8 @@ import torch
 import oracle
 import tp1_skinny_bf16_amd as tp
 import workloads as wl
-from gpu_util import (DEV, candidate_tactics, check_exact, check_random, gpu_run,
-                      sample_rows, say, tactic_label)
+from gpu_util import (DEV, candidate_tactics, check_exact, check_random, gpu_run, say,
+                      tactic_label)
 
 pytestmark = pytest.mark.gpu
 
@@ -80,8 +82,7 @@ def test_full_config_random(name, B):
     plan = tp.Plan(cfg.N, cfg.K, cfg.batches)
     say(f"{name} B={B}: {tactic_label(plan, B)}")
     y = gpu_run(plan, t["x"][:B], Wd)
-    cols = sample_rows(cfg.N, B, cfg.K, budget=3e9, seed=B)
-    check_random(f"{name} B={B}", y, t["x"][:B], t["W"], cols=cols)
+    check_random(f"{name} B={B}", y, t["x"][:B], t["W"])        # every output
 
 
 VERIFY_BINS = [3, 6, 12, 24, 48, 96, 192]   # requests x (1 + speculative tokens)
@@ -98,9 +99,7 @@ def test_verify_step_batches_full_shape(N, K):
     for b in VERIFY_BINS:
         for B in sorted({b, b - 1}):
             y = gpu_run(plan, x[:B], Wd)
-            cols = sample_rows(N, B, K, budget=1.0e9, seed=B)
-            check_exact(f"verify N={N} K={K} B={B} {tactic_label(plan, B)}", y, x[:B], W,
-                        cols=cols)
+            check_exact(f"verify N={N} K={K} B={B} {tactic_label(plan, B)}", y, x[:B], W)
 
 
 @pytest.mark.parametrize("N,K", [(wl.DSA_N, wl.DSA_K), (wl.OPROJ_N, wl.OPROJ_K),
@@ -111,8 +110,7 @@ def test_full_shape_exact_sum_every_planned_tactic(N, K):
     plan = tp.Plan(N, K, BINS)
     for B in BINS:
         y = gpu_run(plan, x[:B], Wd)
-        cols = sample_rows(N, B, K, budget=1.5e9, seed=B)
-        check_exact(f"N={N} K={K} B={B} {tactic_label(plan, B)}", y, x[:B], W, cols=cols)
+        check_exact(f"N={N} K={K} B={B} {tactic_label(plan, B)}", y, x[:B], W)
 
 
 @pytest.mark.parametrize("N,K", [(wl.DSA_N, wl.DSA_K), (wl.OPROJ_N, wl.OPROJ_K),
@@ -181,8 +179,7 @@ def test_determinism_and_invariants():
             assert np.array_equal(wl.from_bits(yn).float().numpy(),
                                   -wl.from_bits(y1).float().numpy()), f"B={B} negation"
         else:
-            cols = sample_rows(N, B, K, budget=1e9, seed=B)
-            check_random(f"B={B} negated x", yn, -x[:B], W, cols=cols)
+            check_random(f"B={B} negated x", yn, -x[:B], W)
         say(f"B={B} deterministic, scaling exact, negation ok ({tactic_label(plan, B)})")
 
 
@@ -240,11 +237,9 @@ def test_multilayer_stream_per_layer_parity():
     for l in range(cfg.layers):
         # each layer is checked on its own GPU input (tolerances scale)
         yi = wl.bits(y_in[l])
-        cols = sample_rows(wl.DSA_N, B, wl.DSA_K, budget=1e9, seed=l)
-        check_random(f"layer {l} in-proj", yi, x_l, t["W_in"][l], cols=cols)
+        check_random(f"layer {l} in-proj", yi, x_l, t["W_in"][l])
         xo = y_in[l][:, :wl.OPROJ_K]
-        cols = sample_rows(wl.OPROJ_N, B, wl.OPROJ_K, budget=1e9, seed=100 + l)
-        check_random(f"layer {l} o_proj", wl.bits(y_o[l]), xo, t["W_o"][l], cols=cols)
+        check_random(f"layer {l} o_proj", wl.bits(y_o[l]), xo, t["W_o"][l])
         x_l = y_o[l]
     say(f"final |y| rms = {float(y_o[-1].float().pow(2).mean().sqrt()):.4g}")
 
@@ -301,11 +296,9 @@ def test_tp_shard_shapes_exact_and_random(N, K):
     plan = tp.Plan(N, K, BINS)
     for B in BINS:
         y = gpu_run(plan, x[:B], Wd)
-        cols = sample_rows(N, B, K, budget=0.6e9, seed=B)
-        check_exact(f"shard N={N} K={K} B={B} {tactic_label(plan, B)}", y, x[:B], W, cols=cols)
+        check_exact(f"shard N={N} K={K} B={B} {tactic_label(plan, B)}", y, x[:B], W)
     x, W = wl.random_case(64, N, K, seed=18)
     Wd = W.to(DEV)
     for B in (1, 16, 64):
         y = gpu_run(plan, x[:B], Wd)
-        cols = sample_rows(N, B, K, budget=0.6e9, seed=100 + B)
-        check_random(f"shard N={N} K={K} B={B} random", y, x[:B], W, cols=cols)
+        check_random(f"shard N={N} K={K} B={B} random", y, x[:B], W)

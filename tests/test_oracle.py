@@ -19,14 +19,12 @@ def _round(mutant=0):
     return lambda v: oracle.round_bf16(v, mutant=mutant)
 
 
-@pytest.mark.parametrize("pin", [p for p in pins.ALL_PINS if p is not pins.invariants],
-                         ids=lambda p: p.__name__)
+@pytest.mark.parametrize("pin", pins.ALL_PINS, ids=lambda p: p.__name__)
 def test_oracle_pin(pin):
-    pin(_proj(), _round())
-
-
-def test_oracle_invariants():
-    pins.invariants(_proj(), _round(), proj_sum=_proj_sum())
+    if pin in (pins.invariants, pins.unrounded_sum):
+        pin(_proj(), _round(), proj_sum=_proj_sum())
+    else:
+        pin(_proj(), _round())
 
 
 def test_thread_count_does_not_change_result():
@@ -50,14 +48,15 @@ def test_strided_rows_and_empty_shapes():
 
 # A planted mistake in the oracle (compiled in with -DORACLE_MUTANT=n) must
 # fail at least one pin: dropped term, wrong weight index, truncation, ties
-# away from zero, float accumulator, wrong x row, double rounding via float.
-@pytest.mark.parametrize("mutant", [1, 2, 3, 4, 5, 6, 7])
+# away from zero, float accumulator, wrong x row, double rounding via float,
+# unrounded sums stored transposed (only the S output is wrong there).
+@pytest.mark.parametrize("mutant", [1, 2, 3, 4, 5, 6, 7, 8])
 def test_pins_catch_planted_mistake(mutant):
     oracle_build.build(mutant)
     failures = []
     for pin in pins.ALL_PINS:
         try:
-            if pin is pins.invariants:
+            if pin in (pins.invariants, pins.unrounded_sum):
                 pin(_proj(mutant), _round(mutant), proj_sum=_proj_sum(mutant))
             elif pin is pins.one_hot:
                 pin(_proj(mutant), _round(mutant), shapes=((640, 256), (256, 384)))
@@ -66,3 +65,6 @@ def test_pins_catch_planted_mistake(mutant):
         except AssertionError:
             failures.append(pin.__name__)
     assert failures, f"mutant {mutant} passed every pin"
+    if mutant == 8:
+        # the rounded outputs are untouched; only the sum pin can see it
+        assert "unrounded_sum" in failures, failures

@@ -1,21 +1,36 @@
 """Benchmark of the TP1 decode projection on one MI355X.
 
-Default run: the o_proj sweep workload (W 7168 x 12288 BF16, x[B, 12288],
-B = 1, 2, 4, 8, 16, seed 1).  One step = one projection call per batch size,
-each on its own weight copy from a rotation of distinct copies (>= 1 GB in
-total, so no call finds its weight in the 256 MB MALL).  Inputs are resident
-in HBM before timing starts.  Prints ONE JSON line:
-  value        = algorithmic HBM bytes of a step / step time, GB/s
-  roofline     = the dominant kernel's achieved GB/s against the 8 TB/s peak
-  read_ceiling = a plain streaming read of the same weight copies, one launch
-                 per copy, and of a 2 GB buffer, measured after the timed
-                 region; the dominant kernel as a fraction of the former
-  cpu_baseline = the CPU oracle timed on a bounded sample of the same step
+Default run (prints ONE JSON line):
 
-`--report PATH` also times every point of every configuration (DSA B=1, the
-o_proj, KDA and DSA sweeps, the 8-layer stream), the plain streaming-read
-ceiling and the cache-assisted ("hot", one weight repeated) figures, and
-writes them as JSON to PATH.
+* Headline: the multi-layer decode stream, the largest single-GPU workload
+  of the five: 8 layers, each a distinct input-projection weight W_in
+  [14560, 7168] then a distinct o_proj weight W_o [7168, 12288] (3.08 GB of
+  weights in all, far more than the 256 MB MALL), B = 64, the o_proj input
+  being columns 0..12287 of the in-projection output, x0 [64, 7168].  All
+  inputs are the seeded recipe of `workloads.config_tensors` (seed 4), the
+  same tensors the GPU parity tests check.  One step = one pass of the
+  chain (16 projection calls on one stream, enqueued by one native call).
+    value     = algorithmic bytes of a step (W + x + y of each call, once)
+                / host-timed seconds per step, GB/s
+    roofline  = the step's dominant kernel (the projection family with the
+                most time per step), its algorithmic bytes per launch over
+                its average launch time, both measured live here with HIP
+                events on the launch stream, against the 8 TB/s HBM peak
+    kernels   = both projections' average launch time and rate
+* per_config: every batch point of the other four workloads (DSA B=1, the
+  o_proj sweep, the KDA sweep, the DSA sweep to B=256), each call on a
+  distinct weight copy from a rotation of >= 1 GB (cold: no call finds its
+  weight in the MALL): us per call back to back (one pair of events around
+  the calls) and by per-call event pairs (median), GB/s and % of 8 TB/s;
+  TFLOP/s and % of the 2.5 PFLOP/s BF16 MFMA peak for B >= 64.
+* read_ceiling: the library's streaming-read probe over the chain's weights
+  back to back and over a 2 GB buffer (the box's plain read rates).
+* cpu_baseline: the CPU oracle (FP64 sums) on the same chain, on all host
+  cores, over a bounded number of layers; its CPU model; and a one-thread
+  figure for the DSA B=1 workload.
+
+`--report PATH` also writes every point's hot figure (one weight repeated,
+cache-assisted) and the graph-replayed chain to PATH as JSON.
 """
 from __future__ import annotations
 
@@ -29,7 +44,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-HEADLINE = "oproj_sweep"
+METRIC = "µs/call + achieved HBM GB/s (% of peak), TP1 BF16 decode projections, B=1..64"
+SWEEPS = ("dsa_b1", "oproj_sweep", "kda_sweep", "dsa_sweep")
 
 
 def _args():
@@ -40,17 +56,24 @@ def _args():
     ap.add_argument("--warm-seconds", type=float, default=0.3,
                     help="after the warmup steps, keep stepping (untimed) until this much "
                          "time has passed, so the timed steps do not run at ramping clocks")
-    ap.add_argument("--report", default=None, help="write the all-config report here")
+    ap.add_argument("--report", default=None,
+                    help="also write hot figures and the graph-replayed chain here")
     ap.add_argument("--configs", default=None,
-                    help="with --report: comma-separated configuration names to time "
-                         "(default all, with the read ceiling and the multi-layer chain)")
+                    help="comma-separated workloads for per_config (default: all four); "
+                         "'none' skips them")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="time only the multi-layer stream (e.g. under a profiler)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="wall time of the bounded oracle sample (whole steps)")
+                    help="wall time of the bounded oracle sample (whole layers)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy 5 times, the known-size "
                          "reference that scales FETCH_SIZE / WRITE_SIZE counters")
     return ap.parse_args()
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
 
 
 def copy_calibration(torch):
@@ -63,111 +86,6 @@ def copy_calibration(torch):
         dst.copy_(src)
     torch.cuda.synchronize()
     _say("copy calibration: 5 x 268435456-byte device copies done")
-
-
-def _say(*a):
-    print(*a, file=sys.stderr, flush=True)
-
-
-def headline(args, torch, tp, wl, timing):
-    cfg = wl.BY_NAME[HEADLINE]
-    t = wl.config_tensors(cfg)
-    dev = torch.device("cuda:0")
-    W0 = t["W"].to(dev)
-    x = t["x"].to(dev)
-    copies = timing.rotation_copies(W0)
-    plan = tp.Plan(cfg.N, cfg.K, cfg.batches)
-    outs = {B: torch.empty((B, cfg.N), dtype=torch.bfloat16, device=dev) for B in cfg.batches}
-    stream = torch.cuda.current_stream()
-    sh = stream.cuda_stream
-    xs = {B: x[:B] for B in cfg.batches}
-    nb = len(cfg.batches)
-    ncopy = len(copies)
-
-    def call(i, B):
-        W = copies[i % ncopy]
-        rc = plan.run_ptr(B, xs[B].data_ptr(), cfg.K, W.data_ptr(), outs[B].data_ptr(), sh)
-        if rc != 0:
-            raise tp.ProjError(rc, f"proj_run B={B}")
-
-    def step(s):
-        for j, B in enumerate(cfg.batches):
-            call(s * nb + j, B)
-
-    for s in range(args.warmup):
-        step(s)
-    # A fresh process starts at low clocks; a few ms of warm-up steps do not
-    # raise them.  Keep stepping, untimed, until warm_seconds have passed.
-    t_warm = time.perf_counter()
-    s = args.warmup
-    while time.perf_counter() - t_warm < args.warm_seconds:
-        for _ in range(20):
-            step(s)
-            s += 1
-        torch.cuda.synchronize()
-    # Timed region: the K steps' calls, grouped by batch size (B-major) so that
-    # each size's K calls run back to back between one pair of HIP events on
-    # the launch stream; a step is still one call per batch size.
-    ev = {B: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-          for B in cfg.batches}
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for j, B in enumerate(cfg.batches):
-        ev[B][0].record(stream)
-        for s in range(args.steps):
-            call(s * nb + j, B)
-        ev[B][1].record(stream)
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms_per_step = elapsed * 1e3 / args.steps
-    step_bytes = sum(wl.algorithmic_bytes(B, cfg.N, cfg.K) for B in cfg.batches)
-    value = step_bytes / (ms_per_step * 1e-3) / 1e9
-
-    per_b = {}
-    for j, B in enumerate(cfg.batches):
-        mean = ev[B][0].elapsed_time(ev[B][1]) * 1e3 / args.steps
-        tac, _ = plan.tactic(B)
-        per_b[B] = {"us_per_call": round(mean, 2),
-                    "GBps": round(timing.gbs(wl.algorithmic_bytes(B, cfg.N, cfg.K), mean), 1),
-                    "kernel": plan.kernel_name(B), "tactic": tac.as_dict()}
-    # dominant kernel: the one with the largest share of the step's GPU time
-    by_kernel = {}
-    for B, r in per_b.items():
-        k = by_kernel.setdefault(r["kernel"], {"us": 0.0, "bytes": 0, "calls": 0})
-        k["us"] += r["us_per_call"]
-        k["bytes"] += wl.algorithmic_bytes(B, cfg.N, cfg.K)
-        k["calls"] += 1
-    name, k = max(by_kernel.items(), key=lambda kv: kv[1]["us"])
-    avg_us = k["us"] / k["calls"]
-    bytes_per_launch = k["bytes"] / k["calls"]
-    achieved = timing.gbs(bytes_per_launch, avg_us)
-    roof = {"bound": "hbm", "kernel": name, "achieved": round(achieved, 1),
-            "peak": timing.HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / timing.HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(name),
-            "avg_launch_us": round(avg_us, 2), "bytes_per_launch": int(bytes_per_launch)}
-    # Read ceilings of the box, after the timed region: the library's
-    # streaming-read probe (a plain 128-bit read-and-reduce, 4 waves per CU)
-    # over the same rotated weight copies back to back, one launch per copy
-    # (what a single-pass projection of this weight can reach per launch),
-    # and over one 2 GB buffer (the sustained rate).
-    sink = torch.empty(65536, dtype=torch.float32, device=dev)
-    wbytes = cfg.N * cfg.K * 2
-    rl = timing.time_calls([(lambda W=W: tp.read_probe(W, sink, 4)) for W in copies],
-                           warmup=2, reps=4 * ncopy, warm_seconds=0.05)
-    big = torch.ones(1024 ** 3, dtype=torch.bfloat16, device=dev)
-    rs = timing.time_calls([lambda: tp.read_probe(big, sink, 4)], warmup=2, reps=10,
-                           warm_seconds=0.05)
-    per_launch = timing.gbs(wbytes, rl["us_mean_b2b"])
-    ceiling = {"per_launch_GBps": round(per_launch, 1),
-               "per_launch_us": round(rl["us_mean_b2b"], 2),
-               "sustained_GBps": round(timing.gbs(big.numel() * 2, rs["us_median"]), 1),
-               "dominant_kernel_frac_of_per_launch": round(achieved / per_launch, 4)}
-    del big
-    res = {"cfg": cfg, "t": t, "plan": plan, "value": value, "ms": ms_per_step,
-           "per_b": per_b, "roofline": roof, "step_bytes": step_bytes,
-           "copies": ncopy, "read_ceiling": ceiling}
-    return res
 
 
 def measured_traffic(kernel: str):
@@ -191,121 +109,225 @@ def measured_traffic(kernel: str):
     return int(total)
 
 
-def cpu_baseline(args, cfg, t, wl):
-    import oracle
-    xb = wl.bits(t["x"])
-    wb = wl.bits(t["W"])
-    threads = oracle.default_threads()
-    oracle.proj(xb[:1], wb[:64], threads=threads)       # load / warm the library
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        for B in cfg.batches:
-            oracle.proj(xb[:B], wb, threads=threads)
-        reps += 1
-        if time.perf_counter() - t0 >= args.cpu_seconds or reps >= 1000:
-            break
-    el = time.perf_counter() - t0
-    step_bytes = sum(wl.algorithmic_bytes(B, cfg.N, cfg.K) for B in cfg.batches)
-    return {"value": round(step_bytes * reps / el / 1e9, 3), "unit": "GB/s",
-            "cores": threads, "kind": "oracle",
-            "sample": f"{reps} full steps of the o_proj sweep (B=1,2,4,8,16 on one "
-                      f"7168x12288 weight), {el:.1f} s, FP64 accumulation",
-            "ms_per_step": round(el * 1e3 / reps, 1)}
+def _events(torch, n):
+    return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
 
 
-def report(args, torch, tp, wl, timing):
-    """Every configuration point, cold (rotated weights) and hot."""
+def headline(args, torch, tp, wl, timing):
+    """The multi-layer stream on the seed-4 tensors."""
+    cfg = wl.BY_NAME["multilayer"]
+    t = wl.config_tensors(cfg)
     dev = torch.device("cuda:0")
-    out = {"points": [], "device": torch.cuda.get_device_name(0)}
-    names = set(args.configs.split(",")) if args.configs else None
-    unknown = (names or set()) - set(wl.BY_NAME)
+    B, L = cfg.bmax, cfg.layers
+    w_in = [w.to(dev) for w in t["W_in"]]
+    w_o = [w.to(dev) for w in t["W_o"]]
+    x0 = t["x"].to(dev)
+    pin = tp.Plan(wl.DSA_N, wl.DSA_K, [B])
+    po = tp.Plan(wl.OPROJ_N, wl.OPROJ_K, [B])
+    stack = tp.LayerStack(pin, po, w_in, w_o)
+    y_in, y_o = stack.buffers(B)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        stack.run(x0, y_in, y_o)
+
+    for _ in range(args.warmup):
+        step()
+    t_warm = time.perf_counter()
+    while time.perf_counter() - t_warm < args.warm_seconds:
+        for _ in range(5):
+            step()
+        torch.cuda.synchronize()
+    e0, e1 = _events(torch, 2)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(args.steps):
+        step()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    gpu_ms_per_step = e0.elapsed_time(e1) / args.steps
+    b_in = wl.algorithmic_bytes(B, wl.DSA_N, wl.DSA_K)
+    b_o = wl.algorithmic_bytes(B, wl.OPROJ_N, wl.OPROJ_K)
+    step_bytes = L * (b_in + b_o)
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    # Each projection family alone, in the chain's own launch configuration:
+    # the 8 layers' calls back to back on the launch stream (distinct weights,
+    # each call's own chain input), one pair of events around args.steps
+    # rounds of them.
+    sh = stream.cuda_stream
+    xin = [x0] + [y_o[l - 1] for l in range(1, L)]
+
+    def run_in(l):
+        rc = pin.run_ptr(B, xin[l].data_ptr(), wl.DSA_K, w_in[l].data_ptr(),
+                         y_in[l].data_ptr(), sh)
+        if rc != 0:
+            raise tp.ProjError(rc, "in-projection")
+
+    def run_o(l):
+        rc = po.run_ptr(B, y_in[l].data_ptr(), wl.DSA_N, w_o[l].data_ptr(),
+                        y_o[l].data_ptr(), sh)
+        if rc != 0:
+            raise tp.ProjError(rc, "o_proj")
+
+    fam = {}
+    for name, fn, nbytes, plan, N, K in (("in_proj", run_in, b_in, pin, wl.DSA_N, wl.DSA_K),
+                                          ("o_proj", run_o, b_o, po, wl.OPROJ_N, wl.OPROJ_K)):
+        for l in range(L):
+            fn(l)
+        torch.cuda.synchronize()
+        a, b = _events(torch, 2)
+        a.record(stream)
+        for _ in range(args.steps):
+            for l in range(L):
+                fn(l)
+        b.record(stream)
+        torch.cuda.synchronize()
+        us = a.elapsed_time(b) * 1e3 / (args.steps * L)
+        fam[name] = {"kernel": plan.kernel_name(B), "shape": f"{N}x{K}", "B": B,
+                     "us_per_launch": round(us, 2), "bytes_per_launch": nbytes,
+                     "GBps": round(timing.gbs(nbytes, us), 1),
+                     "pct_peak": round(100 * timing.gbs(nbytes, us) / timing.HBM_PEAK_GBS, 1),
+                     "TFLOPs": round(2.0 * B * N * K / (us * 1e-6) / 1e12, 1)}
+    # restore the chain's outputs (the per-family passes rewrote them in place
+    # with the same values, in the same order, so this is only for clarity)
+    step()
+    torch.cuda.synchronize()
+    dom_name = max(fam, key=lambda k: fam[k]["us_per_launch"])
+    dom = fam[dom_name]
+    achieved = timing.gbs(dom["bytes_per_launch"], dom["us_per_launch"])
+    roof = {"bound": "hbm", "kernel": dom["kernel"], "role": dom_name,
+            "achieved": round(achieved, 1), "peak": timing.HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / timing.HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic(dom["kernel"]),
+            "avg_launch_us": dom["us_per_launch"],
+            "bytes_per_launch": dom["bytes_per_launch"]}
+
+    # read ceilings: the chain's own weights read back to back by the plain
+    # streaming-read probe (one launch per weight), and a 2 GB buffer
+    sink = torch.empty(65536, dtype=torch.float32, device=dev)
+    rl = timing.time_calls([(lambda W=W: tp.read_probe(W, sink, 4)) for W in w_in],
+                           warmup=2, reps=4 * L, warm_seconds=0.05)
+    big = torch.ones(1024 ** 3, dtype=torch.bfloat16, device=dev)
+    rs = timing.time_calls([lambda: tp.read_probe(big, sink, 4)], warmup=2, reps=10,
+                           warm_seconds=0.05)
+    wbytes = wl.DSA_N * wl.DSA_K * 2
+    per_launch = timing.gbs(wbytes, rl["us_mean_b2b"])
+    ceiling = {"in_proj_weight_read_us": round(rl["us_mean_b2b"], 2),
+               "in_proj_weight_read_GBps": round(per_launch, 1),
+               "sustained_2GB_GBps": round(timing.gbs(big.numel() * 2, rs["us_median"]), 1)}
+    del big
+    graph = None
+    if args.report:
+        graph = timing.time_graph([step], replays=10)
+    return {"cfg": cfg, "t": t, "value": value, "ms": ms_per_step,
+            "gpu_ms": gpu_ms_per_step, "step_bytes": step_bytes, "families": fam,
+            "roofline": roof, "read_ceiling": ceiling, "graph_us": graph,
+            "stack": stack, "tensors": (w_in, w_o, x0, y_in, y_o)}
+
+
+def per_config(args, torch, tp, wl, timing, report):
+    """Every batch point of the four single-projection workloads, cold."""
+    dev = torch.device("cuda:0")
+    names = SWEEPS if args.configs is None else \
+        tuple(n for n in args.configs.split(",") if n and n != "none")
+    unknown = set(names) - set(SWEEPS)
     if unknown:
-        raise SystemExit(f"unknown configurations: {sorted(unknown)}")
-    if names is None:
-        # plain streaming-read ceiling over a 2 GB buffer
-        buf = torch.empty(2 * 1024 ** 3 // 2, dtype=torch.bfloat16, device=dev)
-        buf.fill_(1.0)
-        sink = torch.empty(65536, dtype=torch.float32, device=dev)
-        probe = {}
-        for wpc in (4, 8, 16, 32):
-            r = timing.time_calls([lambda: tp.read_probe(buf, sink, wpc)], warmup=3, reps=20)
-            probe[wpc] = round(timing.gbs(buf.numel() * 2, r["us_median"]), 1)
-        out["read_ceiling_GBps"] = probe
-        _say(f"read ceiling (GB/s by waves/CU): {probe}")
-        del buf
-    for cfg in wl.CONFIGS:
-        if cfg.layers > 1 or (names is not None and cfg.name not in names):
-            continue
+        raise SystemExit(f"unknown workloads: {sorted(unknown)}")
+    out = {}
+    for name in names:
+        cfg = wl.BY_NAME[name]
         t = wl.config_tensors(cfg)
         W0 = t["W"].to(dev)
         x = t["x"].to(dev)
         copies = timing.rotation_copies(W0)
         plan = tp.Plan(cfg.N, cfg.K, cfg.batches)
+        pts = {}
         for B in cfg.batches:
             y = torch.empty((B, cfg.N), dtype=torch.bfloat16, device=dev)
             xb = x[:B]
             calls = [(lambda W=W: plan.run(xb, W, y)) for W in copies]
             cold = timing.time_calls(calls, warmup=3, reps=60)
-            hot = timing.time_calls([lambda: plan.run(xb, W0, y)], warmup=3, reps=30)
             nbytes = wl.algorithmic_bytes(B, cfg.N, cfg.K)
-            tac, _ = plan.tactic(B)
-            p = {"config": cfg.name, "N": cfg.N, "K": cfg.K, "B": B,
-                 "us_median": round(cold["us_median"], 2), "us_p10": round(cold["us_p10"], 2),
-                 "us_p90": round(cold["us_p90"], 2), "us_b2b": round(cold["us_mean_b2b"], 2),
-                 "GBps": round(timing.gbs(nbytes, cold["us_median"]), 1),
-                 "pct_peak": round(100 * timing.gbs(nbytes, cold["us_median"]) / timing.HBM_PEAK_GBS, 1),
-                 "hot_us": round(hot["us_median"], 2),
-                 "TFLOPs": round(2.0 * B * cfg.N * cfg.K / (cold["us_median"] * 1e-6) / 1e12, 1),
-                 "kernel": plan.kernel_name(B), "tactic": tac.as_dict()}
-            out["points"].append(p)
-            _say(f"{cfg.name:12s} B={B:3d} {p['us_median']:8.2f} us {p['GBps']:8.1f} GB/s "
-                 f"{p['pct_peak']:5.1f}% hot {p['hot_us']:7.2f} us  {p['kernel']}")
-        del copies, W0, x, t
+            b2b = cold["us_mean_b2b"]
+            p = {"us_b2b": round(b2b, 2), "us_median": round(cold["us_median"], 2),
+                 "GBps_b2b": round(timing.gbs(nbytes, b2b), 1),
+                 "pct_peak_b2b": round(100 * timing.gbs(nbytes, b2b) / timing.HBM_PEAK_GBS, 1),
+                 "pct_peak_median": round(100 * timing.gbs(nbytes, cold["us_median"])
+                                          / timing.HBM_PEAK_GBS, 1),
+                 "kernel": plan.kernel_name(B)}
+            if B >= 64:
+                tf = 2.0 * B * cfg.N * cfg.K / (b2b * 1e-6) / 1e12
+                p["TFLOPs_b2b"] = round(tf, 1)
+                p["pct_mfma_peak_b2b"] = round(100 * tf / timing.MFMA_BF16_PEAK_TFLOPS, 1)
+            if report is not None:
+                hot = timing.time_calls([lambda: plan.run(xb, W0, y)], warmup=3, reps=30)
+                p["hot_us_median"] = round(hot["us_median"], 2)
+            pts[str(B)] = p
+            _say(f"{name:12s} B={B:3d} b2b {p['us_b2b']:7.2f} us {p['GBps_b2b']:7.1f} GB/s "
+                 f"({p['pct_peak_b2b']:4.1f}%)  per call {p['us_median']:7.2f} us  "
+                 f"{p['kernel']}")
+        out[name] = {"N": cfg.N, "K": cfg.K, "seed": cfg.seed, "weight_copies": len(copies),
+                     "points": pts}
+        del copies, W0, x, t, plan
         torch.cuda.empty_cache()
-    if names is not None and "multilayer" not in names:
-        with open(args.report, "w") as f:
-            json.dump(out, f, indent=1)
-        return
-    # multi-layer stream: 8 x (in-proj 14560x7168 -> o_proj 7168x12288), B = 64
-    cfg = wl.BY_NAME["multilayer"]
-    g = torch.Generator(device=dev)
-    g.manual_seed(cfg.seed)
-    w_in = [(torch.randn((wl.DSA_N, wl.DSA_K), generator=g, device=dev) * 0.02).to(torch.bfloat16)
-            for _ in range(cfg.layers)]
-    w_o = [(torch.randn((wl.OPROJ_N, wl.OPROJ_K), generator=g, device=dev) * 0.02).to(torch.bfloat16)
-           for _ in range(cfg.layers)]
-    x0 = torch.randn((cfg.bmax, wl.DSA_K), generator=g, device=dev).to(torch.bfloat16)
-    pin = tp.Plan(wl.DSA_N, wl.DSA_K, [cfg.bmax])
-    po = tp.Plan(wl.OPROJ_N, wl.OPROJ_K, [cfg.bmax])
-    stack = tp.LayerStack(pin, po, w_in, w_o)
-    y_in, y_o = stack.buffers(cfg.bmax)
-    r = timing.time_calls([lambda: stack.run(x0, y_in, y_o)], warmup=3, reps=20)
-    nbytes = cfg.layers * (wl.algorithmic_bytes(cfg.bmax, wl.DSA_N, wl.DSA_K)
-                           + wl.algorithmic_bytes(cfg.bmax, wl.OPROJ_N, wl.OPROJ_K))
-    out["multilayer"] = {"layers": cfg.layers, "B": cfg.bmax, "us_median": round(r["us_median"], 1),
-                         "GBps": round(timing.gbs(nbytes, r["us_median"]), 1),
-                         "bytes": nbytes, "in_kernel": pin.kernel_name(cfg.bmax),
-                         "o_kernel": po.kernel_name(cfg.bmax)}
-    # the same chain captured once as a graph and replayed (the launches of
-    # all 2 x 8 projections, split-K passes included, submitted as one)
-    side = torch.cuda.Stream()
-    side.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(side):
-        stack.run(x0, y_in, y_o)
-    torch.cuda.current_stream().wait_stream(side)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(graph):
-        stack.run(x0, y_in, y_o)
-    torch.cuda.synchronize()
-    rg = timing.time_calls([graph.replay], warmup=3, reps=20)
-    out["multilayer"].update({"graph_us_median": round(rg["us_median"], 1),
-                              "graph_GBps": round(timing.gbs(nbytes, rg["us_median"]), 1)})
-    del graph
-    _say(f"multilayer 8x(in+o) B=64: {out['multilayer']}")
-    with open(args.report, "w") as f:
-        json.dump(out, f, indent=1)
     return out
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(args, h, wl):
+    """The oracle on the multi-layer stream, layer by layer, chained on its
+    own outputs, until cpu_seconds have passed; and one thread on DSA B=1."""
+    import oracle
+    cfg, t = h["cfg"], h["t"]
+    threads = oracle.default_threads()
+    xb = wl.bits(t["x"])
+    oracle.proj(xb[:1], wl.bits(t["W_in"][0])[:64], threads=threads)   # load the library
+    b_in = wl.algorithmic_bytes(cfg.bmax, wl.DSA_N, wl.DSA_K)
+    b_o = wl.algorithmic_bytes(cfg.bmax, wl.OPROJ_N, wl.OPROJ_K)
+    done, nbytes, x = 0, 0, xb
+    t0 = time.perf_counter()
+    while True:
+        l = done % cfg.layers
+        if l == 0:
+            x = xb
+        yi = oracle.proj(x, wl.bits(t["W_in"][l]), threads=threads)
+        yo = oracle.proj(yi[:, :wl.OPROJ_K], wl.bits(t["W_o"][l]), threads=threads)
+        x = yo
+        done += 1
+        nbytes += b_in + b_o
+        if time.perf_counter() - t0 >= args.cpu_seconds or done >= 4 * cfg.layers:
+            break
+    el = time.perf_counter() - t0
+    # one thread, DSA B=1 (the first workload)
+    c1 = wl.config_tensors(wl.BY_NAME["dsa_b1"])
+    x1, w1 = wl.bits(c1["x"]), wl.bits(c1["W"])
+    t1 = time.perf_counter()
+    oracle.proj(x1, w1, threads=1)
+    e1 = time.perf_counter() - t1
+    n1 = wl.algorithmic_bytes(1, wl.DSA_N, wl.DSA_K)
+    return {"value": round(nbytes / el / 1e9, 3), "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "cpu_model": _cpu_model(),
+            "sample": f"{done} layers (in-projection then o_proj, B=64) of the 8-layer "
+                      f"stream on the seed-4 tensors, chained on the oracle's own outputs, "
+                      f"{el:.1f} s, FP64 sums",
+            "ms_per_layer": round(el * 1e3 / done, 1),
+            "ms_per_step_extrapolated": round(el * 1e3 / done * cfg.layers, 1),
+            "t1_dsa_b1": {"threads": 1, "ms_per_call": round(e1 * 1e3, 1),
+                          "GBps": round(n1 / e1 / 1e9, 3)}}
 
 
 def main():
@@ -325,23 +347,23 @@ def main():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
     torch.cuda.set_device(0)
-    if args.report and args.configs:
-        # a report of selected configurations only (e.g. under a counter run):
-        # no headline steps, so every dispatch belongs to the named points
-        report(args, torch, tp, wl, timing)
-        return
+    _say("timing the 8-layer stream (seed-4 tensors)")
     h = headline(args, torch, tp, wl, timing)
+    _say(f"8-layer stream: {h['ms'] * 1e3:.1f} us/step, {h['value']:.1f} GB/s; "
+         f"{h['families']}")
+    report = {} if args.report else None
+    pc = None
+    if not args.headline_only and args.configs != "none":
+        pc = per_config(args, torch, tp, wl, timing, report)
     cpu = None
-    if not args.no_cpu:
-        cpu = cpu_baseline(args, h["cfg"], h["t"], wl)
-    if args.report:
-        report(args, torch, tp, wl, timing)
+    if not args.no_cpu and not args.headline_only:
+        _say("timing the CPU oracle")
+        cpu = cpu_baseline(args, h, wl)
     if args.copy_calibration:
         copy_calibration(torch)
     cfg = h["cfg"]
     line = {
-        "metric": "achieved HBM GB/s (algorithmic W+x+y bytes / time), TP1 BF16 decode "
-                  "projection, o_proj sweep",
+        "metric": METRIC,
         "value": round(h["value"], 1),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -349,22 +371,32 @@ def main():
         "warmup": args.warmup,
         "warm_seconds": args.warm_seconds,
         "ms_per_step": round(h["ms"], 4),
+        "gpu_ms_per_step": round(h["gpu_ms"], 4),
+        "us_per_call": round(h["ms"] * 1e3 / (2 * cfg.layers), 2),
+        "pct_peak": round(100 * h["value"] / timing.HBM_PEAK_GBS, 1),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "o_proj sweep: W 7168x12288 BF16 ~N(0,0.02), x[B,12288] ~N(0,1), "
-                               "B in {1,2,4,8,16}, seed 1; one call per B per step",
-                   "N": cfg.N, "K": cfg.K, "batches": list(cfg.batches),
-                   "weight_copies": h["copies"], "step_bytes": h["step_bytes"]},
-        "per_batch_us": {str(B): r["us_per_call"] for B, r in h["per_b"].items()},
-        "per_batch_GBps": {str(B): r["GBps"] for B, r in h["per_b"].items()},
-        "kernels": {str(B): r["kernel"] for B, r in h["per_b"].items()},
+        "config": {"workload": "multi-layer decode stream: 8 layers x (W_in 14560x7168 then "
+                               "W_o 7168x12288, distinct BF16 ~N(0,0.02) weights, 3.08 GB), "
+                               "B=64, o_proj input = columns 0..12287 of the in-projection "
+                               "output, x0[64,7168] ~N(0,1), seed 4; one step = the chain",
+                   "layers": cfg.layers, "B": cfg.bmax, "step_bytes": h["step_bytes"],
+                   "calls_per_step": 2 * cfg.layers},
+        "kernels": h["families"],
         "roofline": h["roofline"],
         "read_ceiling": h["read_ceiling"],
+        "per_config": pc,
         "cpu_baseline": cpu,
     }
+    if args.report:
+        report["headline"] = {k: line[k] for k in ("value", "ms_per_step", "kernels")}
+        report["graph_replayed_chain_us"] = h["graph_us"]
+        report["per_config"] = pc
+        with open(args.report, "w") as f:
+            json.dump(report, f, indent=1)
     print(json.dumps(line), flush=True)
 
 

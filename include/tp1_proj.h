@@ -44,17 +44,15 @@ enum proj_status {
     PROJ_ENODEV = -6   /* the plan was built host-only and cannot run      */
 };
 
-/* Kernel families a tactic can name. */
+/* Kernel families a tactic can name (values 2 and 4 named two earlier MFMA
+ * kernels that no measured tactic chose; they are no longer built and a
+ * tactic naming them is refused). */
 enum proj_kernel {
     PROJ_KERNEL_STREAM = 1, /* split-K weight stream: VALU dot products,
                                lanes along K, wavefront reductions         */
-    PROJ_KERNEL_MFMA = 2,   /* BF16 MFMA tiles (16x16x32), FP32 accumulate */
     PROJ_KERNEL_STREAM_DOT2 = 3, /* the weight stream with v_dot2 BF16 pair
                                products: FP32 accumulation whose additions
                                are not always IEEE round-to-nearest      */
-    PROJ_KERNEL_MFMA_LDS = 4, /* MFMA tiles fed from a per-wave LDS tile that
-                               the weight reaches with 1 KB row loads
-                               (bcap 16 or 32, rows 1 or 2)              */
     PROJ_KERNEL_MFMA_XS = 5, /* x and W chunk tiles staged once per
                                workgroup in LDS and shared by its 4 waves
                                (bcap 16..256; rows = 16-row N tiles per
@@ -91,11 +89,11 @@ enum proj_kernel {
  *   bcap   : batch capacity of the kernel instance (>= the bin)
  *   split  : number of K slices S; S > 1 adds a fixed-order reduction pass
  *   rows   : STREAM: W rows a wave carries per pass (1, 2 or 4)
- *            MFMA:   16-column N tiles per wave (1, 2 or 4; 1 at bcap 256)
- *   waves  : waves per workgroup (STREAM 1..8, MFMA 1..4, and MFMA partial
- *            tiles must fit the LDS: waves * 2 * bcap/16 * rows KB <= 160)
+ *            MFMA_XS, MFMA_PIPE: 16-row weight tiles per group
+ *   waves  : STREAM: waves per workgroup (1..8)
+ *            MFMA_XS, MFMA_PIPE: waves along the batch
  *   wpc    : STREAM: waves per compute unit the grid is sized for
- *            MFMA:   0 = one wave per N range (grid from N), else as STREAM
+ *            MFMA_XS, MFMA_PIPE: workgroups per compute unit (1 or 2)
  *   kc     : MFMA_XS, MFMA_PIPE: K chunk staged per step (32..512);
  *            0 elsewhere
  *   depth  : MFMA_XS: chunks loaded into registers ahead of the one being
@@ -223,7 +221,8 @@ int proj_plan_set_tactic(proj_plan_t *plan, int bin,
 /*
  * proj_plan_kernel_name -- the kernel instance(s) proj_run launches for
  * batch B, as they appear in a profiler's kernel trace, e.g.
- * "stream_kernel<1, 1, 16>" or "mfma_kernel<1, 2, 6>+splitk_reduce".
+ * "stream_kernel<1, 4, 16, false>" or
+ * "mfma_pipe_kernel<4, 8, 4, 1, 128, 3, 8>+splitk_reduce4".
  * Writes a NUL-terminated string of at most len bytes into buf.
  */
 int proj_plan_kernel_name(const proj_plan_t *plan, int B, char *buf, size_t len);

@@ -90,14 +90,6 @@ def candidate_tactics(N: int, K: int, bin_: int):
                     for waves, wpc in ((4, 8), (2, 4), (8, 16), (1, 1), (3, 5)):
                         out.append(tp.Tactic(tp.KERNEL_STREAM, bc, split, rows, waves, wpc))
                     out.append(tp.Tactic(tp.KERNEL_STREAM_DOT2, bc, split, rows, 4, 8))
-    if bin_ <= 32:
-        for bc in (16, 32):
-            if bc < bin_:
-                continue
-            for rows in (1, 2):
-                for split in (1, 2):
-                    for waves, wpc in ((4, 0), (2, 3), (1, 8), (3, 4)):
-                        out.append(tp.Tactic(tp.KERNEL_MFMA_LDS, bc, split, rows, waves, wpc))
     for bc, shapes in ((16, ((4, 1, 128, 1), (4, 1, 256, 2), (4, 1, 512, 1), (8, 1, 128, 2),
                              (16, 1, 128, 1))),
                        (32, ((4, 1, 128, 2), (4, 2, 128, 1), (8, 2, 256, 1))),
@@ -129,13 +121,4 @@ def candidate_tactics(N: int, K: int, bin_: int):
                     if wpc == 1:  # the same with a staggered chunk order
                         out.append(tp.Tactic(tp.KERNEL_MFMA_PIPE, bc, split, rows, waves, wpc,
                                              kc, depth, kw, nw, stagger=1))
-    for bc in (16, 32, 64, 128, 256):
-        if bc < bin_:
-            continue
-        for rows in (1, 2, 4):
-            if bc == 256 and rows > 1:
-                continue
-            for split in (1, 2):
-                for waves, wpc in ((4, 0), (2, 3), (1, 8), (3, 4)):
-                    out.append(tp.Tactic(tp.KERNEL_MFMA, bc, split, rows, waves, wpc))
     return out

@@ -112,8 +112,8 @@ def test_set_tactic_validation():
     for bad in [tp.Tactic(tp.KERNEL_STREAM, 1, 1, 3, 4, 8),       # no instance
                 tp.Tactic(tp.KERNEL_STREAM, 1, 1, 1, 9, 8),       # too many waves
                 tp.Tactic(tp.KERNEL_STREAM, 1, 0, 1, 4, 8),       # split 0
-                tp.Tactic(tp.KERNEL_MFMA, 8, 1, 1, 4, 0),         # no MFMA bcap 8
-                tp.Tactic(tp.KERNEL_MFMA, 256, 1, 2, 4, 0),       # too many acc regs
+                tp.Tactic(2, 16, 1, 1, 4, 0),                     # retired kernel ids
+                tp.Tactic(4, 16, 1, 1, 2, 4),
                 tp.Tactic(7, 1, 1, 1, 1, 1)]:
         with pytest.raises(tp.ProjError):
             p.set_tactic(1, bad)
@@ -125,6 +125,21 @@ def test_set_tactic_validation():
     q = tp.Plan(7168, 12288, [8], host_only=True)
     with pytest.raises(tp.ProjError):
         q.set_tactic(8, tp.Tactic(tp.KERNEL_STREAM, 8, 1, 1, 4, 8))
+
+
+def test_stream_lds_counts_the_static_partials():
+    """The stream kernel keeps [8 waves][2][rows * bcap] floats of static LDS
+    beside the staged x slice: a slice whose staged x alone fills the LDS
+    exactly is refused at plan time instead of failing at launch."""
+    # bcap 8, one 10240-wide slice: 8 * 10240 * 2 = 163840 bytes of x = all of it
+    p = tp.Plan(1000, 10240, [8], host_only=True)
+    with pytest.raises(tp.ProjError):
+        p.set_tactic(8, tp.Tactic(tp.KERNEL_STREAM, 8, 1, 4, 4, 8))
+    # two slices of 5120 leave room for the partials
+    p.set_tactic(8, tp.Tactic(tp.KERNEL_STREAM, 8, 2, 4, 4, 8))
+    # a slice of 10240 - 512 = 9728 for bcap 8: 155648 + 2048 + 16 bytes fit
+    q = tp.Plan(1000, 19456, [8], host_only=True)
+    q.set_tactic(8, tp.Tactic(tp.KERNEL_STREAM, 8, 2, 4, 4, 8))
 
 
 def test_run_argument_checks_on_a_host_only_plan():
@@ -208,8 +223,6 @@ def test_stagger_is_validated():
                                      stagger=2)),
                       (16, tp.Tactic(tp.KERNEL_MFMA_PIPE, 16, 1, 4, 1, 1, 256, 3, 2, 8,
                                      stagger=-1)),
-                      (16, tp.Tactic(tp.KERNEL_MFMA_LDS, 16, 1, 1, 2, 4, stagger=1)),
-                      (16, tp.Tactic(tp.KERNEL_MFMA, 16, 1, 2, 4, 0, stagger=1)),
                       (1, tp.Tactic(tp.KERNEL_STREAM, 1, 1, 4, 4, 8, stagger=1))]:
         with pytest.raises(tp.ProjError):
             p.set_tactic(bin_, bad)

@@ -256,8 +256,6 @@ def test_fused_split_matches_two_pass_bitwise():
     twop = tp.Plan(N, K, [4, 16, 64])
     tactics = [(4, tp.Tactic(tp.KERNEL_STREAM, 4, 3, 2, 4, 8)),
                (4, tp.Tactic(tp.KERNEL_STREAM_DOT2, 4, 2, 4, 2, 4)),
-               (16, tp.Tactic(tp.KERNEL_MFMA_LDS, 16, 2, 1, 2, 4)),
-               (16, tp.Tactic(tp.KERNEL_MFMA, 16, 3, 2, 4, 0)),
                (16, tp.Tactic(tp.KERNEL_MFMA_XS, 16, 4, 8, 1, 2, 128, 1)),
                (64, tp.Tactic(tp.KERNEL_MFMA_XS, 64, 3, 4, 4, 2, 128, 1)),
                (16, tp.Tactic(tp.KERNEL_MFMA_PIPE, 16, 4, 4, 1, 2, 128, 4, 1, 4)),

@@ -7,8 +7,8 @@ of the vLLM API page "vllm.models.kimi_k3.nvidia.specialized_decode.runtime.dep"
 kernels behind the C ABI of include/tp1_proj.h; this package is the thin
 Python binding (torch supplies device memory and streams only).
 """
-from ._binding import (EXPORTS, KERNEL_IDS, KERNEL_MFMA, KERNEL_NAMES,  # noqa: F401
-                       KERNEL_MFMA_LDS, KERNEL_MFMA_PIPE, KERNEL_MFMA_XS, KERNEL_STREAM,
+from ._binding import (EXPORTS, KERNEL_IDS, KERNEL_NAMES,  # noqa: F401
+                       KERNEL_MFMA_PIPE, KERNEL_MFMA_XS, KERNEL_STREAM,
                        KERNEL_STREAM_DOT2,
                        LIB_PATH, MAX_BATCH, MAX_BATCHES, PROJ_EALIGN, PROJ_EBATCH,
                        PROJ_EHIP, PROJ_EINVAL, PROJ_ENODEV, PROJ_ENOMEM, PROJ_OK,

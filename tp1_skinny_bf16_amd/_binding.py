@@ -23,14 +23,11 @@ PROJ_ENOMEM = -5
 PROJ_ENODEV = -6
 
 KERNEL_STREAM = 1
-KERNEL_MFMA = 2
 KERNEL_STREAM_DOT2 = 3
-KERNEL_MFMA_LDS = 4
 KERNEL_MFMA_XS = 5
 KERNEL_MFMA_PIPE = 6
-KERNEL_NAMES = {KERNEL_STREAM: "stream", KERNEL_MFMA: "mfma", KERNEL_STREAM_DOT2: "stream_dot2",
-                KERNEL_MFMA_LDS: "mfma_lds", KERNEL_MFMA_XS: "mfma_xs",
-                KERNEL_MFMA_PIPE: "mfma_pipe"}
+KERNEL_NAMES = {KERNEL_STREAM: "stream", KERNEL_STREAM_DOT2: "stream_dot2",
+                KERNEL_MFMA_XS: "mfma_xs", KERNEL_MFMA_PIPE: "mfma_pipe"}
 KERNEL_IDS = {v: k for k, v in KERNEL_NAMES.items()}
 
 PLAN_HOST_ONLY = 0x1

@@ -14,10 +14,6 @@
 //                  multiply-adds, then a fixed-order DPP reduction across the
 //                  64 lanes.  Each wave owns a contiguous range of rows and
 //                  keeps a ring of weight loads in flight across rows.
-//   mfma_kernel    larger batches.  v_mfma_f32_16x16x32_bf16 tiles with x as
-//                  the A operand (batch rows) and W as the B operand (output
-//                  columns), both loaded straight into registers in operand
-//                  layout, FP32 accumulators.
 //   mfma_xs_kernel / mfma_pipe_kernel  a workgroup shares one x tile and
 //                  one weight tile per K chunk in LDS; the pipe variant
 //                  fills a ring of LDS stages with direct-to-LDS loads several
@@ -389,24 +385,12 @@ __global__ __launch_bounds__(512) void stream_kernel(StreamArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// MFMA kernel (larger batches).
-// v_mfma_f32_16x16x32_bf16 operand layout: lane l supplies row (l % 16) of
-// the A operand and column (l % 16) of the B operand, each with 8 K values
-// of K group (l / 16); the accumulator lane l holds rows 4*(l/16) + 0..3 of
-// column l % 16.  The K order inside a group only permutes the sum, so each
-// lane simply loads 8 consecutive K of its row.  x is the A operand (MT
-// tiles of 16 batch rows), W the B operand (NT tiles of 16 output columns).
-//
-// Work is split as in the stream kernel: workgroup g owns rows
-// [N*g/G, N*(g+1)/G) for one K slice, cut into groups of 16*NT rows; the
-// (group, 32-wide K step) sequence is split evenly over the waves, each
-// wave a contiguous run.  A group a wave covers entirely is written out; a
-// group cut by a wave boundary leaves per-wave partial tiles in LDS that
-// are added in wave order after one barrier.  W loads here are ordinary
-// cached loads: each instruction reads 64 B of each of 16 rows, and the
-// other half of every 128 B line is read by the next step, so keeping the
-// line in cache pays.  Rows past B or past the workgroup's rows are clamped
-// onto valid data and their results discarded.
+// MFMA operand layout (v_mfma_f32_16x16x32_bf16): lane l supplies row
+// (l % 16) of the A operand and column (l % 16) of the B operand, each with 8
+// K values of K group (l / 16); the accumulator lane l holds rows
+// 4*(l/16) + 0..3 of column l % 16.  The K order inside a group only permutes
+// the sum, so a lane takes 8 consecutive K of its row.  x is the A operand
+// (tiles of 16 batch rows), W the B operand (tiles of 16 output columns).
 // ---------------------------------------------------------------------------
 struct MfmaArgs {
     const uint16_t *x;
@@ -420,339 +404,6 @@ struct MfmaArgs {
     int S;
     int stagger;  // 1: workgroup b starts at chunk b mod C of its slice (XS, PIPE)
 };
-
-template <int MT, int NT, int P>
-__global__ __launch_bounds__(256) void mfma_kernel(MfmaArgs a) {
-    extern __shared__ __align__(16) float mpart[];  // [wave][2][MT*NT][64][4]
-    const int lane = threadIdx.x & 63;
-    const int NW = uniform(blockDim.x >> 6);
-    const int wave = uniform(threadIdx.x >> 6);
-    const int s = blockIdx.y;
-    const int k0 = s * a.ks;
-    const int klen = min(a.K - k0, a.ks);
-    const int row0 = (int)((long)a.N * blockIdx.x / gridDim.x);
-    const int rows = (int)((long)a.N * (blockIdx.x + 1) / gridDim.x) - row0;
-    constexpr int GR = 16 * NT;                // rows (output columns) per group
-    const int C = (klen + 31) >> 5;            // 32-wide K steps per group
-    const int Gb = (rows + GR - 1) / GR;
-    const int Tb = Gb * C;
-    const int q0 = (int)((long)Tb * wave / NW);
-    const int q1 = (int)((long)Tb * (wave + 1) / NW);
-    const int T = q1 - q0;
-    const bool ragged = (klen & 31) != 0;
-    const int lrow = lane & 15, lgrp = lane >> 4;
-
-    const uint16_t *xrow[MT];
-#pragma unroll
-    for (int m = 0; m < MT; ++m)
-        xrow[m] = a.x + (size_t)min(m * 16 + lrow, a.B - 1) * a.ldx + k0;
-    const uint16_t *wblk = a.W + (size_t)row0 * a.K + k0;
-    float *mine_part = mpart + (size_t)wave * 2 * MT * NT * 256;
-
-    auto store_out = [&](int row, int col, float v) {
-        if (a.S == 1)
-            a.y[(size_t)row * a.N + col] = to_bf16(v);
-        else
-            store_partial(a.ws + ((size_t)s * a.B + row) * a.N + col, v, a.cnt != nullptr);
-    };
-
-    if (T > 0) {
-        u32x4 wb[P][NT];
-        u32x4 xb[P][MT];
-        f32x4 acc[MT][NT];
-#pragma unroll
-        for (int m = 0; m < MT; ++m)
-#pragma unroll
-            for (int n = 0; n < NT; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-        int lt = 0, lg = q0 / C, lc = q0 - (q0 / C) * C;
-        auto load_step = [&](u32x4 (&w)[NT], u32x4 (&xx)[MT]) {
-            const int kk = min(lc * 32 + lgrp * 8, klen - 8);
-#pragma unroll
-            for (int n = 0; n < NT; ++n) {
-                const int r = min(lg * GR + n * 16 + lrow, rows - 1);
-                w[n] = load_cached(wblk + (size_t)r * a.K + kk);
-            }
-#pragma unroll
-            for (int m = 0; m < MT; ++m) xx[m] = load_cached(xrow[m] + kk);
-            if (lt < T - 1) {
-                ++lt;
-                if (++lc == C) { lc = 0; ++lg; }
-            }
-        };
-
-#pragma unroll
-        for (int j = 0; j < P; ++j) load_step(wb[j], xb[j]);
-
-        int cg = q0 / C, cc = q0 - (q0 / C) * C;
-        for (int t0 = 0; t0 < T; t0 += P) {
-#pragma unroll
-            for (int j = 0; j < P; ++j) {
-                if (t0 + j < T) {
-                    u32x4 w[NT];
-#pragma unroll
-                    for (int n = 0; n < NT; ++n) w[n] = wb[j][n];
-                    if (ragged && cc == C - 1) {
-                        const bool dead = cc * 32 + lgrp * 8 >= klen;  // past the slice
-#pragma unroll
-                        for (int n = 0; n < NT; ++n)
-                            w[n] = dead ? u32x4{0u, 0u, 0u, 0u} : w[n];
-                    }
-#pragma unroll
-                    for (int m = 0; m < MT; ++m)
-#pragma unroll
-                        for (int n = 0; n < NT; ++n)
-                            acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                __builtin_bit_cast(bf16x8_t, xb[j][m]),
-                                __builtin_bit_cast(bf16x8_t, w[n]), acc[m][n], 0, 0, 0);
-                }
-                load_step(wb[j], xb[j]);
-                if (t0 + j < T) {
-                    if (cc == C - 1 || t0 + j == T - 1) {
-                        const bool started_here = cg * C >= q0;
-                        if (cc == C - 1 && started_here) {
-#pragma unroll
-                            for (int m = 0; m < MT; ++m)
-#pragma unroll
-                                for (int n = 0; n < NT; ++n) {
-                                    const int r = cg * GR + n * 16 + lrow;
-#pragma unroll
-                                    for (int v = 0; v < 4; ++v) {
-                                        const int b = m * 16 + lgrp * 4 + v;
-                                        if (b < a.B && r < rows) store_out(b, row0 + r, acc[m][n][v]);
-                                    }
-                                }
-                        } else {
-                            float *slot = mine_part + (started_here ? 1 : 0) * MT * NT * 256;
-#pragma unroll
-                            for (int m = 0; m < MT; ++m)
-#pragma unroll
-                                for (int n = 0; n < NT; ++n)
-                                    *reinterpret_cast<f32x4 *>(slot + ((m * NT + n) * 64 + lane) * 4) =
-                                        acc[m][n];
-                        }
-#pragma unroll
-                        for (int m = 0; m < MT; ++m)
-#pragma unroll
-                            for (int n = 0; n < NT; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-                    }
-                    if (++cc == C) { cc = 0; ++cg; }
-                }
-            }
-        }
-    }
-
-    // Groups cut by a wave boundary: add the partial tiles in wave order.
-    __syncthreads();
-    constexpr int TILE = MT * NT * 256;  // floats of one partial
-    for (int i = 1; i < NW; ++i) {
-        const int qi = (int)((long)Tb * i / NW);
-        const int qp = (int)((long)Tb * (i - 1) / NW);
-        const int g = qi / C;
-        const bool split = qi < Tb && (qi - g * C) != 0;
-        const bool seen = i > 1 && qp / C == g && (qp - (qp / C) * C) != 0;
-        if (!split || seen) continue;
-        const int wlo = wave_of_step(g * C, Tb, NW);
-        const int whi = wave_of_step(g * C + C - 1, Tb, NW);
-        for (int e = threadIdx.x; e < TILE; e += blockDim.x) {
-            float sum = 0.f;
-            for (int v = wlo; v <= whi; ++v) {
-                const int qv = (int)((long)Tb * v / NW);
-                const int qv1 = (int)((long)Tb * (v + 1) / NW);
-                if (qv == qv1) continue;
-                sum += mpart[((size_t)v * 2 + (g * C < qv ? 0 : 1)) * TILE + e];
-            }
-            // e = ((m*NT + n)*64 + l)*4 + vv
-            const int vv = e & 3, l = (e >> 2) & 63, mn = e >> 8;
-            const int m = mn / NT, n = mn - (mn / NT) * NT;
-            const int r = g * GR + n * 16 + (l & 15);
-            const int b = m * 16 + (l >> 4) * 4 + vv;
-            if (b < a.B && r < rows) store_out(b, row0 + r, sum);
-        }
-    }
-    if (a.S > 1 && a.cnt) splitk_fixup(a.ws, a.y, a.cnt, a.N, a.B, row0, rows);
-}
-
-// ---------------------------------------------------------------------------
-// LDS-transposed MFMA kernel (mid batches).
-// The weight is read exactly as in the stream kernel -- lanes along K, each
-// load 1 KB of one row -- for a group of 16*NT rows and a 512-wide K chunk,
-// then written to a padded per-wave LDS tile and read back in MFMA B-operand
-// layout (lane (n, g) reads row n, K 32j + 8g..+7 of the chunk; the 1040-byte
-// row pitch puts the 16 rows of a read in distinct banks).  x (the A
-// operand, MT tiles of 16 batch rows) is read with ordinary cached loads,
-// one chunk ahead.  Work split, partial-tile combine and clamping are as in
-// mfma_kernel; a step here is one (group, chunk).
-// ---------------------------------------------------------------------------
-constexpr int kTilePitch = 520;  // bf16 elements per LDS tile row (1040 B)
-
-template <int MT, int NT>
-__global__ __launch_bounds__(256) void mfma_lds_kernel(MfmaArgs a) {
-    extern __shared__ __align__(16) float tl_lds[];
-    constexpr int GR = 16 * NT;
-    const int lane = threadIdx.x & 63;
-    const int NW = uniform(blockDim.x >> 6);
-    const int wave = uniform(threadIdx.x >> 6);
-    const int s = blockIdx.y;
-    const int k0 = s * a.ks;
-    const int klen = min(a.K - k0, a.ks);
-    const int row0 = (int)((long)a.N * blockIdx.x / gridDim.x);
-    const int rows = (int)((long)a.N * (blockIdx.x + 1) / gridDim.x) - row0;
-    const int C = (klen + 511) >> 9;           // 512-wide chunks per group
-    const int Gb = (rows + GR - 1) / GR;
-    const int Tb = Gb * C;
-    const int q0 = (int)((long)Tb * wave / NW);
-    const int q1 = (int)((long)Tb * (wave + 1) / NW);
-    const int T = q1 - q0;
-    const bool ragged = (klen & 511) != 0;
-    const int lrow = lane & 15, lgrp = lane >> 4;
-    const int lk = lane * 8;
-
-    // LDS: per-wave tiles, then per-wave partial slots.
-    uint16_t *tile = reinterpret_cast<uint16_t *>(tl_lds) + (size_t)wave * GR * kTilePitch;
-    float *parts = tl_lds + (size_t)NW * GR * kTilePitch / 2;
-    constexpr int TILE = MT * NT * 256;  // floats of one partial
-    float *mine_part = parts + (size_t)wave * 2 * TILE;
-
-    const uint16_t *xrow[MT];
-#pragma unroll
-    for (int m = 0; m < MT; ++m)
-        xrow[m] = a.x + (size_t)min(m * 16 + lrow, a.B - 1) * a.ldx + k0 + lgrp * 8;
-    const uint16_t *wblk = a.W + (size_t)row0 * a.K + k0;
-
-    auto store_out = [&](int row, int col, float v) {
-        if (a.S == 1)
-            a.y[(size_t)row * a.N + col] = to_bf16(v);
-        else
-            store_partial(a.ws + ((size_t)s * a.B + row) * a.N + col, v, a.cnt != nullptr);
-    };
-
-    if (T > 0) {
-        u32x4 wr[GR];        // this step's weight rows (lanes along K)
-        u32x4 xr[16][MT];    // this step's A fragments, 16 K steps of 32
-        f32x4 acc[MT][NT];
-#pragma unroll
-        for (int m = 0; m < MT; ++m)
-#pragma unroll
-            for (int n = 0; n < NT; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-        int lt = 0, lg = q0 / C, lc = q0 - (q0 / C) * C;
-        auto load_w = [&]() {
-            const int kk = min(lc * 512 + lk, klen - 8);
-#pragma unroll
-            for (int r = 0; r < GR; ++r) {
-                const int row = min(lg * GR + r, rows - 1);
-                wr[r] = load_stream(wblk + (size_t)row * a.K + kk);
-            }
-        };
-        auto load_x = [&](int j) {
-            const int kk = min(lc * 512 + j * 32, klen - 8 - lgrp * 8);
-#pragma unroll
-            for (int m = 0; m < MT; ++m) xr[j][m] = load_cached(xrow[m] + kk);
-        };
-        auto advance = [&]() {
-            if (lt < T - 1) {
-                ++lt;
-                if (++lc == C) { lc = 0; ++lg; }
-            }
-        };
-        load_w();
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int j = 0; j < 16; ++j) load_x(j);
-        __builtin_amdgcn_sched_barrier(0);
-        advance();
-
-        int cg = q0 / C, cc = q0 - (q0 / C) * C;
-        for (int t = 0; t < T; ++t) {
-            // Weight rows of this step -> LDS tile (zeroed past the slice).
-            const bool dead = ragged && cc == C - 1 && cc * 512 + lk >= klen;
-#pragma unroll
-            for (int r = 0; r < GR; ++r)
-                *reinterpret_cast<u32x4 *>(tile + r * kTilePitch + lk) =
-                    dead ? u32x4{0u, 0u, 0u, 0u} : wr[r];
-            // Keep the issue order: this step's tile writes, then the next
-            // step's weight loads, then the A-fragment loads (which are
-            // younger, so waiting for the weight never drains them).
-            __builtin_amdgcn_sched_barrier(0);
-            load_w();  // next step's rows go out while this one computes
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                u32x4 bfr[NT];
-#pragma unroll
-                for (int n = 0; n < NT; ++n)
-                    bfr[n] = *reinterpret_cast<const u32x4 *>(
-                        tile + (n * 16 + lrow) * kTilePitch + j * 32 + lgrp * 8);
-#pragma unroll
-                for (int m = 0; m < MT; ++m)
-#pragma unroll
-                    for (int n = 0; n < NT; ++n)
-                        acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8_t, xr[j][m]),
-                            __builtin_bit_cast(bf16x8_t, bfr[n]), acc[m][n], 0, 0, 0);
-                load_x(j);  // this K step's A fragment for the next step
-            }
-            advance();
-            if (cc == C - 1 || t == T - 1) {
-                const bool started_here = cg * C >= q0;
-                if (cc == C - 1 && started_here) {
-#pragma unroll
-                    for (int m = 0; m < MT; ++m)
-#pragma unroll
-                        for (int n = 0; n < NT; ++n) {
-                            const int r = cg * GR + n * 16 + lrow;
-#pragma unroll
-                            for (int v = 0; v < 4; ++v) {
-                                const int b = m * 16 + lgrp * 4 + v;
-                                if (b < a.B && r < rows) store_out(b, row0 + r, acc[m][n][v]);
-                            }
-                        }
-                } else {
-                    float *slot = mine_part + (started_here ? 1 : 0) * TILE;
-#pragma unroll
-                    for (int m = 0; m < MT; ++m)
-#pragma unroll
-                        for (int n = 0; n < NT; ++n)
-                            *reinterpret_cast<f32x4 *>(slot + ((m * NT + n) * 64 + lane) * 4) =
-                                acc[m][n];
-                }
-#pragma unroll
-                for (int m = 0; m < MT; ++m)
-#pragma unroll
-                    for (int n = 0; n < NT; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
-            }
-            if (++cc == C) { cc = 0; ++cg; }
-        }
-    }
-
-    __syncthreads();
-    for (int i = 1; i < NW; ++i) {
-        const int qi = (int)((long)Tb * i / NW);
-        const int qp = (int)((long)Tb * (i - 1) / NW);
-        const int g = qi / C;
-        const bool split = qi < Tb && (qi - g * C) != 0;
-        const bool seen = i > 1 && qp / C == g && (qp - (qp / C) * C) != 0;
-        if (!split || seen) continue;
-        const int wlo = wave_of_step(g * C, Tb, NW);
-        const int whi = wave_of_step(g * C + C - 1, Tb, NW);
-        for (int e = threadIdx.x; e < TILE; e += blockDim.x) {
-            float sum = 0.f;
-            for (int v = wlo; v <= whi; ++v) {
-                const int qv = (int)((long)Tb * v / NW);
-                const int qv1 = (int)((long)Tb * (v + 1) / NW);
-                if (qv == qv1) continue;
-                sum += parts[((size_t)v * 2 + (g * C < qv ? 0 : 1)) * TILE + e];
-            }
-            const int vv = e & 3, l = (e >> 2) & 63, mn = e >> 8;
-            const int m = mn / NT, n = mn - (mn / NT) * NT;
-            const int r = g * GR + n * 16 + (l & 15);
-            const int b = m * 16 + (l >> 4) * 4 + vv;
-            if (b < a.B && r < rows) store_out(b, row0 + r, sum);
-        }
-    }
-    if (a.S > 1 && a.cnt) splitk_fixup(a.ws, a.y, a.cnt, a.N, a.B, row0, rows);
-}
 
 // ---------------------------------------------------------------------------
 // Shared-tile MFMA kernel (large batches).
@@ -1214,24 +865,17 @@ int *fused_counters(const LaunchShape &sh, long gx, int S) {
     return (S > 1 && sh.cnt && gx <= kSplitCounters) ? sh.cnt : nullptr;
 }
 
-// Workgroups per K slice of a launch (gridDim.x): wpc waves (STREAM, MFMA,
-// MFMA_LDS) or workgroups (MFMA_XS) per compute unit over the S slices; for
-// MFMA / MFMA_LDS, wpc 0 means one wave per 16*rows-row group.  At most one
-// workgroup per row.
+// Workgroups per K slice of a launch (gridDim.x): wpc waves (STREAM) or
+// workgroups (MFMA_XS, MFMA_PIPE) per compute unit over the S slices.  At
+// most one workgroup per row.
 long grid_x(const LaunchShape &sh, const proj_tactic_t &t) {
     const int S = slice_count(sh.K, t);
     long g;
     if (t.kernel == PROJ_KERNEL_STREAM || t.kernel == PROJ_KERNEL_STREAM_DOT2) {
         const int nw = std::min(t.waves, kStreamMaxWaves);
         g = (long)sh.num_cus * t.wpc / (nw * (long)S);
-    } else if (t.kernel == PROJ_KERNEL_MFMA_XS || t.kernel == PROJ_KERNEL_MFMA_PIPE) {
-        g = (long)sh.num_cus * std::max(1, t.wpc) / S;
     } else {
-        const int nw = std::min(t.waves, 4);
-        if (t.wpc > 0)
-            g = (long)sh.num_cus * t.wpc / (nw * (long)S);
-        else
-            g = ceil_div_i(ceil_div_i(sh.N, 16 * t.rows), nw);
+        g = (long)sh.num_cus * std::max(1, t.wpc) / S;
     }
     return std::max(1L, std::min(g, (long)sh.N));
 }
@@ -1242,11 +886,6 @@ constexpr int stream_ring(int BC, int R) {
     return (BC >= 8 ? 8 : (BC >= 4 ? 12 : 16)) / R > 1
                ? (BC >= 8 ? 8 : (BC >= 4 ? 12 : 16)) / R
                : 2;
-}
-
-// Steps of loads in flight for the MFMA kernel (fewer as operands grow).
-constexpr int mfma_ring(int MT, int NT) {
-    return MT + NT <= 2 ? 8 : (MT + NT <= 3 ? 6 : (MT + NT <= 5 ? 4 : (MT + NT <= 8 ? 2 : 1)));
 }
 
 template <int BC, int R, bool D2>
@@ -1265,45 +904,6 @@ hipError_t launch_stream_inst(const LaunchShape &sh, const proj_tactic_t &t,
     hipLaunchKernelGGL((stream_kernel<BC, R, P, D2>), dim3((unsigned)g, S), dim3(nw * 64), lds,
                        stream, a);
     return hipGetLastError();
-}
-
-template <int MT, int NT>
-hipError_t launch_mfma_inst(const LaunchShape &sh, const proj_tactic_t &t,
-                            hipStream_t stream) {
-    constexpr int P = mfma_ring(MT, NT);
-    const int ks = slice_len(sh.K, t);
-    const int S = slice_count(sh.K, t);
-    const int nw = std::min(t.waves, 4);
-    const long g = grid_x(sh, t);
-    const size_t lds = (size_t)nw * 2 * MT * NT * 256 * sizeof(float);
-    MfmaArgs a{sh.x, sh.ldx, sh.W, sh.y, sh.ws, fused_counters(sh, g, S), sh.N, sh.K, sh.B,
-               ks, S};
-    hipLaunchKernelGGL((mfma_kernel<MT, NT, P>), dim3((unsigned)g, S), dim3(nw * 64), lds,
-                       stream, a);
-    return hipGetLastError();
-}
-
-template <int MT, int NT>
-hipError_t launch_mfma_lds_inst(const LaunchShape &sh, const proj_tactic_t &t,
-                                hipStream_t stream) {
-    const int ks = slice_len(sh.K, t);
-    const int S = slice_count(sh.K, t);
-    const int nw = std::min(t.waves, 4);
-    const long g = grid_x(sh, t);
-    const size_t lds = mfma_lds_tile_bytes(t);
-    MfmaArgs a{sh.x, sh.ldx, sh.W, sh.y, sh.ws, fused_counters(sh, g, S), sh.N, sh.K, sh.B,
-               ks, S};
-    hipLaunchKernelGGL((mfma_lds_kernel<MT, NT>), dim3((unsigned)g, S), dim3(nw * 64), lds,
-                       stream, a);
-    return hipGetLastError();
-}
-
-hipError_t launch_mfma_lds(const LaunchShape &sh, const proj_tactic_t &t, hipStream_t st) {
-    if (t.bcap == 16 && t.rows == 1) return launch_mfma_lds_inst<1, 1>(sh, t, st);
-    if (t.bcap == 16 && t.rows == 2) return launch_mfma_lds_inst<1, 2>(sh, t, st);
-    if (t.bcap == 32 && t.rows == 1) return launch_mfma_lds_inst<2, 1>(sh, t, st);
-    if (t.bcap == 32 && t.rows == 2) return launch_mfma_lds_inst<2, 2>(sh, t, st);
-    return hipErrorInvalidValue;
 }
 
 template <int MT, int NTB, int WM, int KC, int PD>
@@ -1372,18 +972,6 @@ hipError_t launch_stream(const LaunchShape &sh, const proj_tactic_t &t,
     return hipErrorInvalidValue;
 }
 
-hipError_t launch_mfma(const LaunchShape &sh, const proj_tactic_t &t, hipStream_t st) {
-#define TP1_MFMA_CASE(BC, NT) \
-    if (t.bcap == BC && t.rows == NT) return launch_mfma_inst<BC / 16, NT>(sh, t, st);
-    TP1_MFMA_CASE(16, 1) TP1_MFMA_CASE(16, 2) TP1_MFMA_CASE(16, 4)
-    TP1_MFMA_CASE(32, 1) TP1_MFMA_CASE(32, 2) TP1_MFMA_CASE(32, 4)
-    TP1_MFMA_CASE(64, 1) TP1_MFMA_CASE(64, 2) TP1_MFMA_CASE(64, 4)
-    TP1_MFMA_CASE(128, 1) TP1_MFMA_CASE(128, 2) TP1_MFMA_CASE(128, 4)
-    TP1_MFMA_CASE(256, 1)
-#undef TP1_MFMA_CASE
-    return hipErrorInvalidValue;
-}
-
 }  // namespace
 
 hipError_t launch_projection(const LaunchShape &sh, const proj_tactic_t &t,
@@ -1391,10 +979,6 @@ hipError_t launch_projection(const LaunchShape &sh, const proj_tactic_t &t,
     hipError_t e;
     if (t.kernel == PROJ_KERNEL_STREAM || t.kernel == PROJ_KERNEL_STREAM_DOT2)
         e = launch_stream(sh, t, stream);
-    else if (t.kernel == PROJ_KERNEL_MFMA)
-        e = launch_mfma(sh, t, stream);
-    else if (t.kernel == PROJ_KERNEL_MFMA_LDS)
-        e = launch_mfma_lds(sh, t, stream);
     else if (t.kernel == PROJ_KERNEL_MFMA_XS)
         e = launch_mfma_xs(sh, t, stream);
     else if (t.kernel == PROJ_KERNEL_MFMA_PIPE)
@@ -1429,9 +1013,6 @@ int kernel_name(const LaunchShape &sh, const proj_tactic_t &t, char *buf, size_t
                      stream_ring(t.bcap, t.rows),
                      t.kernel == PROJ_KERNEL_STREAM_DOT2 ? "true" : "false",
                      split ? red : "");
-    else if (t.kernel == PROJ_KERNEL_MFMA_LDS)
-        n = snprintf(buf, len, "mfma_lds_kernel<%d, %d>%s", t.bcap / 16, t.rows,
-                     split ? red : "");
     else if (t.kernel == PROJ_KERNEL_MFMA_XS)
         n = snprintf(buf, len, "mfma_xs_kernel<%d, %d, %d, %d, %d>%s", t.bcap / 16, t.rows,
                      t.waves, t.kc, t.depth, split ? red : "");
@@ -1439,8 +1020,7 @@ int kernel_name(const LaunchShape &sh, const proj_tactic_t &t, char *buf, size_t
         n = snprintf(buf, len, "mfma_pipe_kernel<%d, %d, %d, %d, %d, %d, %d>%s", t.bcap / 16,
                      t.rows, t.waves, t.kw, t.kc, t.depth, t.nw, split ? red : "");
     else
-        n = snprintf(buf, len, "mfma_kernel<%d, %d, %d>%s", t.bcap / 16, t.rows,
-                     mfma_ring(t.bcap / 16, t.rows), split ? red : "");
+        return -1;
     return (n < 0 || (size_t)n >= len) ? -1 : 0;
 }
 
@@ -1473,18 +1053,6 @@ hipError_t allow_dynamic_lds(size_t bytes) {
     TP1_ALLOW_STREAM(4, 1) TP1_ALLOW_STREAM(4, 2) TP1_ALLOW_STREAM(4, 4)
     TP1_ALLOW_STREAM(8, 1) TP1_ALLOW_STREAM(8, 2) TP1_ALLOW_STREAM(8, 4)
 #undef TP1_ALLOW_STREAM
-#define TP1_ALLOW_MFMA(BC, NT) \
-    keep(allow(&mfma_kernel<BC / 16, NT, mfma_ring(BC / 16, NT)>, b));
-    TP1_ALLOW_MFMA(16, 1) TP1_ALLOW_MFMA(16, 2) TP1_ALLOW_MFMA(16, 4)
-    TP1_ALLOW_MFMA(32, 1) TP1_ALLOW_MFMA(32, 2) TP1_ALLOW_MFMA(32, 4)
-    TP1_ALLOW_MFMA(64, 1) TP1_ALLOW_MFMA(64, 2) TP1_ALLOW_MFMA(64, 4)
-    TP1_ALLOW_MFMA(128, 1) TP1_ALLOW_MFMA(128, 2) TP1_ALLOW_MFMA(128, 4)
-    TP1_ALLOW_MFMA(256, 1)
-#undef TP1_ALLOW_MFMA
-    keep(allow(&mfma_lds_kernel<1, 1>, b));
-    keep(allow(&mfma_lds_kernel<1, 2>, b));
-    keep(allow(&mfma_lds_kernel<2, 1>, b));
-    keep(allow(&mfma_lds_kernel<2, 2>, b));
 #define TP1_ALLOW_XS(BC, NTB, WM, KC, PD) \
     keep(allow(&mfma_xs_kernel<BC / 16, NTB, WM, KC, PD>, b));
     TP1_XS_INSTANCES(TP1_ALLOW_XS)

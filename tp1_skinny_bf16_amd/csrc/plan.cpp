@@ -49,15 +49,6 @@ bool tactic_instance_exists(const proj_tactic_t &t) {
     if (t.kernel == PROJ_KERNEL_STREAM || t.kernel == PROJ_KERNEL_STREAM_DOT2)
         return (t.bcap == 1 || t.bcap == 2 || t.bcap == 4 || t.bcap == 8) &&
                (t.rows == 1 || t.rows == 2 || t.rows == 4);
-    if (t.kernel == PROJ_KERNEL_MFMA) {
-        const bool m = t.bcap == 16 || t.bcap == 32 || t.bcap == 64 ||
-                       t.bcap == 128 || t.bcap == 256;
-        const bool n = t.rows == 1 || t.rows == 2 || t.rows == 4;
-        // 256 rows x 2+ N tiles would need 128+ accumulator registers.
-        return m && n && !(t.bcap == 256 && t.rows > 1);
-    }
-    if (t.kernel == PROJ_KERNEL_MFMA_LDS)
-        return (t.bcap == 16 || t.bcap == 32) && (t.rows == 1 || t.rows == 2);
     if (t.kernel == PROJ_KERNEL_MFMA_XS) {
 #define TP1_XS_MATCH(BC, NTB, WM, KC, PD) \
         if (t.bcap == BC && t.rows == NTB && t.waves == WM && t.kc == KC && t.depth == PD) \
@@ -81,10 +72,9 @@ bool tactic_instance_exists(const proj_tactic_t &t) {
 int slice_len(int K, const proj_tactic_t &t) {
     const int S = std::max(1, t.split);
     // K granularity of a slice: one MFMA step, one shared chunk, or 8
-    const int step = t.kernel == PROJ_KERNEL_MFMA ? 32
-                     : (t.kernel == PROJ_KERNEL_MFMA_XS || t.kernel == PROJ_KERNEL_MFMA_PIPE
-                            ? std::max(t.kc, 32)
-                            : 8);
+    const int step = t.kernel == PROJ_KERNEL_MFMA_XS || t.kernel == PROJ_KERNEL_MFMA_PIPE
+                         ? std::max(t.kc, 32)
+                         : 8;
     int ks = ceil_div(K, S);
     ks = ceil_div(ks, step) * step;
     return std::max(ks, step);
@@ -100,6 +90,24 @@ size_t stream_lds_bytes(int K, const proj_tactic_t &t) {
     return (size_t)t.bcap * (size_t)ksp * 2u;
 }
 
+size_t static_lds_bytes(const proj_tactic_t &t) {
+    // every kernel may run the fused split-K reduction, whose flag is one
+    // shared int (16 bytes with alignment); the stream kernel also keeps the
+    // wave-boundary partial sums [8 waves][2][rows * bcap] floats
+    size_t b = 16;
+    if (t.kernel == PROJ_KERNEL_STREAM || t.kernel == PROJ_KERNEL_STREAM_DOT2)
+        b += 8u * 2u * (size_t)t.rows * (size_t)t.bcap * sizeof(float);
+    return b;
+}
+
+size_t dynamic_lds_bytes(int K, const proj_tactic_t &t) {
+    if (t.kernel == PROJ_KERNEL_STREAM || t.kernel == PROJ_KERNEL_STREAM_DOT2)
+        return stream_lds_bytes(K, t);
+    if (t.kernel == PROJ_KERNEL_MFMA_XS) return mfma_xs_lds_bytes(t);
+    if (t.kernel == PROJ_KERNEL_MFMA_PIPE) return mfma_pipe_lds_bytes(t);
+    return 0;
+}
+
 size_t mfma_xs_lds_bytes(const proj_tactic_t &t) {
     return (size_t)(t.bcap + 16 * t.rows) * (size_t)(t.kc + 8) * 2u;
 }
@@ -112,15 +120,6 @@ size_t mfma_pipe_lds_bytes(const proj_tactic_t &t) {
     return ring + parts;
 }
 
-size_t mfma_lds_tile_bytes(const proj_tactic_t &t) {
-    // per wave: a 16*rows x 520 BF16 tile plus two partial tiles
-    return (size_t)t.waves * ((size_t)16 * t.rows * 520 * 2 +
-                              2u * (size_t)(t.bcap / 16) * (size_t)t.rows * 1024u);
-}
-
-size_t mfma_lds_bytes(const proj_tactic_t &t) {
-    return (size_t)t.waves * 2u * (size_t)(t.bcap / 16) * (size_t)t.rows * 1024u;
-}
 
 size_t tactic_workspace(int N, int K, const proj_tactic_t &t) {
     const int S = slice_count(K, t);
@@ -137,25 +136,14 @@ int check_tactic(int N, int K, int bin, const proj_tactic_t &t) {
     if (t.wpc < 0 || t.wpc > 32) return PROJ_EINVAL;
     if (t.kernel == PROJ_KERNEL_STREAM || t.kernel == PROJ_KERNEL_STREAM_DOT2) {
         if (t.wpc < 1 || t.waves > 8) return PROJ_EINVAL;
-        if (stream_lds_bytes(K, t) > kLdsBytes) return PROJ_EINVAL;
     }
-    if (t.kernel == PROJ_KERNEL_MFMA) {
-        if (t.waves > 4) return PROJ_EINVAL;
-        if (mfma_lds_bytes(t) > kLdsBytes) return PROJ_EINVAL;
-    }
-    if (t.kernel == PROJ_KERNEL_MFMA_LDS) {
-        if (t.waves > 4) return PROJ_EINVAL;
-        if (mfma_lds_tile_bytes(t) > kLdsBytes) return PROJ_EINVAL;
-    }
-    if (t.kernel == PROJ_KERNEL_MFMA_XS) {
+    if (t.kernel == PROJ_KERNEL_MFMA_XS || t.kernel == PROJ_KERNEL_MFMA_PIPE) {
         if (t.wpc < 1 || t.wpc > 2) return PROJ_EINVAL;
-        if (mfma_xs_lds_bytes(t) > kLdsBytes) return PROJ_EINVAL;
-    } else if (t.kernel == PROJ_KERNEL_MFMA_PIPE) {
-        if (t.wpc < 1 || t.wpc > 2) return PROJ_EINVAL;
-        if (mfma_pipe_lds_bytes(t) > kLdsBytes) return PROJ_EINVAL;
     } else if (t.kc != 0 || t.depth != 0) {
         return PROJ_EINVAL;
     }
+    // the instance's dynamic and static LDS together fit a workgroup
+    if (dynamic_lds_bytes(K, t) + static_lds_bytes(t) > kLdsBytes) return PROJ_EINVAL;
     if (t.kernel != PROJ_KERNEL_MFMA_PIPE && (t.kw != 0 || t.nw != 0)) return PROJ_EINVAL;
     if (t.stagger != 0 && t.stagger != 1) return PROJ_EINVAL;
     if (t.stagger && t.kernel != PROJ_KERNEL_MFMA_XS && t.kernel != PROJ_KERNEL_MFMA_PIPE)

@@ -92,14 +92,16 @@ int slice_len(int K, const proj_tactic_t &t);
 // Number of K slices actually launched (ceil(K / slice_len)).
 int slice_count(int K, const proj_tactic_t &t);
 
-// LDS bytes of an MFMA_LDS tactic's per-wave tiles and partial tiles.
-size_t mfma_lds_tile_bytes(const proj_tactic_t &t);
-
-// LDS bytes of an MFMA tactic's per-wave partial tiles.
-size_t mfma_lds_bytes(const proj_tactic_t &t);
 
 // LDS bytes a STREAM tactic stages x into.
 size_t stream_lds_bytes(int K, const proj_tactic_t &t);
+
+// Static LDS of a tactic's kernel instance (its __shared__ arrays), which
+// the workgroup's LDS must hold beside the dynamic part.
+size_t static_lds_bytes(const proj_tactic_t &t);
+
+// Dynamic LDS bytes a tactic's kernel instance is launched with.
+size_t dynamic_lds_bytes(int K, const proj_tactic_t &t);
 
 // The tactic for (N, K, bin): the measured table entry when the shape was
 // measured, else the default rule.

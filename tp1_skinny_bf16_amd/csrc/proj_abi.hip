@@ -146,7 +146,7 @@ int proj_plan(int N, int K, const int *batches, int n_batches, unsigned flags,
         proj_tactic_t &t = p->core.tactics[i];
         while ((t.kernel == PROJ_KERNEL_STREAM || t.kernel == PROJ_KERNEL_STREAM_DOT2) &&
                t.split < 64 &&
-               tp1::stream_lds_bytes(K, t) > p->lds_limit)
+               tp1::stream_lds_bytes(K, t) + tp1::static_lds_bytes(t) > p->lds_limit)
             ++t.split;
     }
     rc = alloc_workspace(p, tp1::plan_workspace(p->core));
@@ -196,18 +196,8 @@ int proj_plan_set_tactic(proj_plan_t *plan, int bin, const proj_tactic_t *tactic
     if (i < 0) return PROJ_EINVAL;
     if (tp1::check_tactic(plan->core.N, plan->core.K, bin, *tactic) != PROJ_OK)
         return PROJ_EINVAL;
-    if ((tactic->kernel == PROJ_KERNEL_STREAM || tactic->kernel == PROJ_KERNEL_STREAM_DOT2) &&
-        tp1::stream_lds_bytes(plan->core.K, *tactic) > plan->lds_limit)
-        return PROJ_EINVAL;
-    if (tactic->kernel == PROJ_KERNEL_MFMA && tp1::mfma_lds_bytes(*tactic) > plan->lds_limit)
-        return PROJ_EINVAL;
-    if (tactic->kernel == PROJ_KERNEL_MFMA_LDS &&
-        tp1::mfma_lds_tile_bytes(*tactic) > plan->lds_limit)
-        return PROJ_EINVAL;
-    if (tactic->kernel == PROJ_KERNEL_MFMA_XS && tp1::mfma_xs_lds_bytes(*tactic) > plan->lds_limit)
-        return PROJ_EINVAL;
-    if (tactic->kernel == PROJ_KERNEL_MFMA_PIPE &&
-        tp1::mfma_pipe_lds_bytes(*tactic) > plan->lds_limit)
+    if (tp1::dynamic_lds_bytes(plan->core.K, *tactic) + tp1::static_lds_bytes(*tactic) >
+        plan->lds_limit)
         return PROJ_EINVAL;
     const int rc = alloc_workspace(plan, tp1::tactic_workspace(plan->core.N, plan->core.K, *tactic));
     if (rc != PROJ_OK) return rc;

@@ -28,8 +28,8 @@ import time
 
 import torch
 
-from . import (KERNEL_IDS, KERNEL_MFMA, KERNEL_MFMA_LDS, KERNEL_MFMA_PIPE, KERNEL_MFMA_XS,
-               KERNEL_STREAM, KERNEL_STREAM_DOT2, Plan, ProjError, Tactic)
+from . import (KERNEL_IDS, KERNEL_MFMA_PIPE, KERNEL_MFMA_XS, KERNEL_STREAM,
+               KERNEL_STREAM_DOT2, Plan, ProjError, Tactic)
 from .timing import gbs, rotation_copies, time_calls, time_graph
 
 SHAPES = {"dsa": (14560, 7168), "oproj": (7168, 12288), "kda": (49376, 7168)}
@@ -52,18 +52,6 @@ def candidates(bin_: int, full: bool = False):
             if not full and (waves == 8 and wpc < 8 or split > 2):
                 continue
             out.append(Tactic(kern, bc, split, rows, waves, wpc))
-    if True:
-        bc = max(16, next_pow2(bin_))
-        for rows, split, waves, wpc in itertools.product(
-                (1, 2, 4), (1, 2, 3, 4, 6), (1, 2, 4), (0, 2, 4, 8)):
-            if bc == 256 and rows > 1:
-                continue
-            out.append(Tactic(KERNEL_MFMA, bc, split, rows, waves, wpc))
-    if bin_ <= 32:
-        bc = 16 if bin_ <= 16 else 32
-        for rows, split, waves, wpc in itertools.product(
-                (1, 2), (1, 2), (1, 2, 3, 4), (0, 2, 4, 6, 8, 12)):
-            out.append(Tactic(KERNEL_MFMA_LDS, bc, split, rows, waves, wpc))
     bc = max(16, next_pow2(bin_))
     xs = {16: ((4, 1, 128, 1), (4, 1, 128, 2), (4, 1, 256, 2), (4, 1, 512, 1), (8, 1, 128, 1),
                (8, 1, 128, 2), (8, 1, 256, 1), (16, 1, 128, 1)),
@@ -118,7 +106,7 @@ def _key(res):
 
 
 def measure(N: int, K: int, bins, reps: int = 40, log=None, full: bool = False,
-            fused_split: bool = False, graph: bool = False):
+            fused_split: bool = False, graph: bool = False, only=None):
     dev = torch.device("cuda:0")
     g = torch.Generator(device=dev)
     g.manual_seed(7)
@@ -143,7 +131,13 @@ def measure(N: int, K: int, bins, reps: int = 40, log=None, full: bool = False,
         xb = x[:b]
         st = torch.cuda.current_stream().cuda_stream
         rows = []
-        for t in candidates(b, full):
+        cands = candidates(b, full)
+        if only:
+            # a subset of the kernel families, measured beside the tactic the
+            # library's table gives this bin
+            table_t, _ = Plan(N, K, bins, host_only=True).tactic(b)
+            cands = [table_t] + [t for t in cands if t.kernel_name in only and t != table_t]
+        for t in cands:
             try:
                 plan.set_tactic(b, t)
             except ProjError:
@@ -202,10 +196,8 @@ def table_rows(result) -> str:
             t["kw"] = 1  # measured before the field existed: one wave along K
         if t["kernel"] == "mfma_pipe" and not t.get("nw"):
             t["nw"] = 4  # measured before the field existed: four waves
-        k = {"stream": "PROJ_KERNEL_STREAM", "mfma": "PROJ_KERNEL_MFMA",
-             "stream_dot2": "PROJ_KERNEL_STREAM_DOT2",
-             "mfma_lds": "PROJ_KERNEL_MFMA_LDS", "mfma_xs": "PROJ_KERNEL_MFMA_XS",
-             "mfma_pipe": "PROJ_KERNEL_MFMA_PIPE"}[t["kernel"]]
+        k = {"stream": "PROJ_KERNEL_STREAM", "stream_dot2": "PROJ_KERNEL_STREAM_DOT2",
+             "mfma_xs": "PROJ_KERNEL_MFMA_XS", "mfma_pipe": "PROJ_KERNEL_MFMA_PIPE"}[t["kernel"]]
         lines.append(f"    {{{result['N']}, {result['K']}, {b}, {{{k}, {t['bcap']}, {t['split']}, "
                      f"{t['rows']}, {t['waves']}, {t['wpc']}, {t.get('kc', 0)}, "
                      f"{t.get('depth', 0)}, {t.get('kw', 0)}, {t.get('nw', 0)}, "
@@ -292,6 +284,9 @@ def main():
     ap.add_argument("--graph", action="store_true",
                     help="time each candidate's calls captured in one graph (for kernels "
                          "as short as the host's launch submission)")
+    ap.add_argument("--only", default=None,
+                    help="comma-separated kernel families to measure (e.g. mfma_pipe), beside "
+                         "the table's tactic for each bin")
     ap.add_argument("--out", required=True)
     a = ap.parse_args()
     bins = [int(v) for v in a.bins.split(",")]
@@ -300,7 +295,8 @@ def main():
     for sh in a.shape:
         N, K = SHAPES[sh] if sh in SHAPES else (int(v) for v in sh.split("x"))
         res = measure(N, K, bins, a.reps, log=lambda m: print(m, flush=True), full=a.full,
-                      fused_split=a.fused_split, graph=a.graph)
+                      fused_split=a.fused_split, graph=a.graph,
+                      only=set(a.only.split(",")) if a.only else None)
         allres.append(res)
         print(table_rows(res), flush=True)
         print(f"crossover (first MFMA bin) for {N}x{K}: {res['crossover']}  "

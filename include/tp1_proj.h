@@ -41,7 +41,9 @@ enum proj_status {
     PROJ_EALIGN = -3,  /* x, W or y not 16-byte aligned, or ldx % 8 != 0   */
     PROJ_EHIP = -4,    /* a HIP runtime call failed (no device, launch...) */
     PROJ_ENOMEM = -5,  /* host or device allocation failed                 */
-    PROJ_ENODEV = -6   /* the plan was built host-only and cannot run      */
+    PROJ_ENODEV = -6,  /* the plan was built host-only and cannot run      */
+    PROJ_ESCRATCH = -7 /* proj_run_noalloc: the call needs more split-K
+                          scratch than its static buffer holds (32 MiB)    */
 };
 
 /* Kernel families a tactic can name (values 2 and 4 named two earlier MFMA
@@ -192,6 +194,29 @@ int proj_run(const proj_plan_t *plan, int B, const void *x, long ldx,
 int proj_run_layers(const proj_plan_t *in, const proj_plan_t *out, int L, int B,
                     const void *x0, long ldx0, const void *const *W_in,
                     const void *const *W_o, void *y_in, void *y_o, void *stream);
+
+/*
+ * proj_run_noalloc -- for callers that cannot allocate device memory (code
+ * being captured into a graph, tight serving loops, harnesses that forbid
+ * allocation): proj_run without a plan, allocating nothing.
+ *   N, K, x, ldx, W, y, stream : as for proj_plan / proj_run
+ *   B      : 0 <= B <= 256; the tactic is the one a plan for the batches
+ *            1, 2, 4, ..., 256 would use for B (the smallest power of two
+ *            >= B), taken from the same measured table and default rule
+ * Split-K partial sums go to a fixed 32 MiB device array of the library
+ * (one per GPU, held until the process ends) instead of a plan's workspace;
+ * nothing in it needs to start at zero, since every partial is written
+ * before it is read.  Every call on a GPU shares that GPU's array, so calls
+ * that overlap in time on one GPU (on different streams, or from different
+ * threads) race.  The first call on a device reads its attributes and the
+ * array's address and sets the kernels' LDS allowance; none of this
+ * allocates.  A tactic needing more than 32 MiB of partial sums returns
+ * PROJ_ESCRATCH before any launch (the measured tables stay within 30 MB).
+ * Returns PROJ_OK, PROJ_EINVAL, PROJ_EBATCH, PROJ_EALIGN, PROJ_ESCRATCH or
+ * PROJ_EHIP.
+ */
+int proj_run_noalloc(int N, int K, int B, const void *x, long ldx, const void *W, void *y,
+                     void *stream);
 
 /* proj_free -- release a plan and its workspace.  NULL is a no-op. */
 void proj_free(proj_plan_t *plan);

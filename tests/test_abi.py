@@ -42,7 +42,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_strerror_covers_every_status():
     for code in (tp.PROJ_OK, tp.PROJ_EINVAL, tp.PROJ_EBATCH, tp.PROJ_EALIGN,
-                 tp.PROJ_EHIP, tp.PROJ_ENOMEM, tp.PROJ_ENODEV):
+                 tp.PROJ_EHIP, tp.PROJ_ENOMEM, tp.PROJ_ENODEV, tp.PROJ_ESCRATCH):
         assert tp.strerror(code) and tp.strerror(code) != "unknown status"
     assert tp.strerror(12345) == "unknown status"
 
@@ -260,3 +260,21 @@ def test_split_reduction_pass_named_by_output_count():
     r = tp.Plan(1001, 1024, [16], host_only=True)
     r.set_tactic(16, tp.Tactic(tp.KERNEL_MFMA_PIPE, 16, 1, 4, 1, 1, 128, 4, 1, 4))
     assert "splitk" not in r.kernel_name(16)                # no split, no pass
+
+
+def test_noalloc_argument_checks_return_before_any_device_call():
+    """proj_run_noalloc validates shape, batch, stride, alignment and overlap
+    on the host and returns before touching a device (these calls run here,
+    without a GPU; the pointers are never dereferenced)."""
+    run = tp.run_noalloc_ptr
+    a, b, c = 0x10000, 0x20000000, 0x40000000        # 16-byte aligned, disjoint
+    assert run(0, 64, 1, a, 64, b, c) == tp.PROJ_EINVAL          # N <= 0
+    assert run(100, 60, 1, a, 60, b, c) == tp.PROJ_EINVAL        # K % 8
+    assert run(100, 64, -1, a, 64, b, c) == tp.PROJ_EBATCH
+    assert run(100, 64, 257, a, 64, b, c) == tp.PROJ_EBATCH      # above 256
+    assert run(100, 64, 0, 0, 64, 0, 0) == tp.PROJ_OK            # B == 0: no-op
+    assert run(100, 64, 2, a, 32, b, c) == tp.PROJ_EINVAL        # ldx < K
+    assert run(100, 64, 2, 0, 64, b, c) == tp.PROJ_EINVAL        # null x
+    assert run(100, 64, 2, a + 2, 64, b, c) == tp.PROJ_EALIGN    # misaligned x
+    assert run(100, 64, 2, a, 68, b, c) == tp.PROJ_EALIGN        # ldx % 8
+    assert run(100, 64, 2, a, 64, b, b + 64) == tp.PROJ_EINVAL   # y overlaps W

@@ -21,6 +21,7 @@ PROJ_EALIGN = -3
 PROJ_EHIP = -4
 PROJ_ENOMEM = -5
 PROJ_ENODEV = -6
+PROJ_ESCRATCH = -7
 
 KERNEL_STREAM = 1
 KERNEL_STREAM_DOT2 = 3
@@ -39,7 +40,7 @@ MAX_BATCHES = 64
 EXPORTS = ("proj_plan", "proj_run", "proj_free", "proj_strerror",
            "proj_plan_tactic", "proj_plan_set_tactic",
            "proj_plan_workspace_bytes", "proj_read_probe", "proj_run_layers",
-           "proj_plan_kernel_name")
+           "proj_plan_kernel_name", "proj_run_noalloc")
 
 
 class ProjError(RuntimeError):
@@ -119,6 +120,9 @@ def _lib():
     lib.proj_run_layers.argtypes = [vp, vp, ctypes.c_int, ctypes.c_int, vp, ctypes.c_long,
                                     ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp, vp]
     lib.proj_run_layers.restype = ctypes.c_int
+    lib.proj_run_noalloc.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp,
+                                     ctypes.c_long, vp, vp, vp]
+    lib.proj_run_noalloc.restype = ctypes.c_int
     lib.proj_read_probe.argtypes = [vp, ctypes.c_size_t, vp, ctypes.c_int, vp]
     lib.proj_read_probe.restype = ctypes.c_int
     _LIB = lib
@@ -244,6 +248,33 @@ class Plan:
                           _stream_handle(stream))
         _check(rc, f"proj_run(B={B})")
         return out
+
+
+def run_noalloc_ptr(N: int, K: int, B: int, x_ptr: int, ldx: int, w_ptr: int, y_ptr: int,
+                    stream: int = 0) -> int:
+    """Raw proj_run_noalloc call: returns the status code."""
+    return _lib().proj_run_noalloc(int(N), int(K), int(B), ctypes.c_void_p(x_ptr), int(ldx),
+                                   ctypes.c_void_p(w_ptr), ctypes.c_void_p(y_ptr),
+                                   ctypes.c_void_p(stream))
+
+
+def run_noalloc(x, W, out, *, stream=None):
+    """y[B, N] = x[B, K] . W^T into the preallocated `out`, with no plan and
+    no device allocation (the library's static split-K scratch)."""
+    import torch
+    if x.dtype != torch.bfloat16 or W.dtype != torch.bfloat16 or out.dtype != torch.bfloat16:
+        raise TypeError("x, W and out must be bfloat16")
+    N, K = W.shape
+    B = x.shape[0]
+    if x.dim() != 2 or x.shape[1] != K or x.stride(1) != 1 or not W.is_contiguous():
+        raise ValueError("x must be [B, K] with unit column stride and W contiguous [N, K]")
+    if tuple(out.shape) != (B, N) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous [B, N] tensor")
+    ldx = x.stride(0) if B > 1 else K
+    rc = run_noalloc_ptr(N, K, B, x.data_ptr(), ldx, W.data_ptr(), out.data_ptr(),
+                         _stream_handle(stream))
+    _check(rc, f"proj_run_noalloc(N={N}, K={K}, B={B})")
+    return out
 
 
 def read_probe(buf, sink, waves_per_cu: int = 0, stream=None):

@@ -75,6 +75,55 @@ int prepare_device(int dev, size_t lds) {
     return PROJ_OK;
 }
 
+// Split-K scratch of proj_run_noalloc: a fixed device array, one copy per
+// GPU the library runs on, held until the process ends.  In host code its
+// name is only a stand-in; the device address comes from
+// hipGetSymbolAddress, once per device, and is the only handle used.
+constexpr size_t kNoallocScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) float scratch[kNoallocScratchBytes / sizeof(float)];
+
+struct NoallocDevice {
+    bool ready = false;
+    float *scratch = nullptr;  // device address of `scratch` on this device
+    int num_cus = 0;
+    size_t lds_limit = tp1::kLdsBytes;
+};
+constexpr int kMaxDevices = 64;
+NoallocDevice g_noalloc[kMaxDevices];
+std::mutex g_noalloc_mu;
+
+// First call on a device: its attributes, the kernels' LDS allowance and the
+// scratch address.  Allocates nothing.
+int noalloc_device(int dev, NoallocDevice **out) {
+    if (dev < 0 || dev >= kMaxDevices) return PROJ_EHIP;
+    std::lock_guard<std::mutex> lock(g_noalloc_mu);
+    NoallocDevice &d = g_noalloc[dev];
+    if (!d.ready) {
+        int cus = 0, lds = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) !=
+                hipSuccess ||
+            hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) !=
+                hipSuccess) {
+            (void)hipGetLastError();
+            return PROJ_EHIP;
+        }
+        size_t limit = tp1::kLdsBytes;
+        if (lds > 0 && (size_t)lds < limit) limit = (size_t)lds;
+        if (prepare_device(dev, limit) != PROJ_OK) return PROJ_EHIP;
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) {
+            (void)hipGetLastError();
+            return PROJ_EHIP;
+        }
+        d.scratch = static_cast<float *>(ptr);
+        d.num_cus = cus > 0 ? cus : 256;
+        d.lds_limit = limit;
+        d.ready = true;
+    }
+    *out = &d;
+    return PROJ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -88,6 +137,9 @@ const char *proj_strerror(int code) {
         case PROJ_EHIP: return "HIP runtime error";
         case PROJ_ENOMEM: return "out of memory";
         case PROJ_ENODEV: return "plan was built host-only and cannot run";
+        case PROJ_ESCRATCH:
+            return "the call needs more split-K scratch than the static buffer of "
+                   "proj_run_noalloc holds (32 MiB)";
         default: return "unknown status";
     }
 }
@@ -289,6 +341,55 @@ int proj_run_layers(const proj_plan_t *in, const proj_plan_t *out, int L, int B,
         ldx = b.N;
     }
     return PROJ_OK;
+}
+
+int proj_run_noalloc(int N, int K, int B, const void *x, long ldx, const void *W, void *y,
+                     void *stream) {
+    // the batch list of the page's "_bins" rule here: powers of two to 256
+    static const int kBins[] = {1, 2, 4, 8, 16, 32, 64, 128, 256};
+    constexpr int kNb = (int)(sizeof(kBins) / sizeof(kBins[0]));
+    if (tp1::check_plan_args(N, K, kBins, kNb, 0) != PROJ_OK) return PROJ_EINVAL;
+    if (B < 0 || B > kBins[kNb - 1]) return PROJ_EBATCH;
+    if (ldx == 0) ldx = K;
+    if (ldx < K) return PROJ_EINVAL;
+    if (B == 0) return PROJ_OK;
+    if (!x || !W || !y) return PROJ_EINVAL;
+    if (!aligned16(x) || !aligned16(W) || !aligned16(y) || (ldx % 8) != 0)
+        return PROJ_EALIGN;
+    const uintptr_t yb = reinterpret_cast<uintptr_t>(y);
+    const uintptr_t ye = yb + (uintptr_t)B * N * 2u;
+    const uintptr_t xb = reinterpret_cast<uintptr_t>(x);
+    const uintptr_t xe = xb + ((uintptr_t)(B - 1) * ldx + K) * 2u;
+    const uintptr_t wb = reinterpret_cast<uintptr_t>(W);
+    const uintptr_t we = wb + (uintptr_t)N * K * 2u;
+    if ((yb < xe && xb < ye) || (yb < we && wb < ye)) return PROJ_EINVAL;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return PROJ_EHIP;
+    }
+    NoallocDevice *d = nullptr;
+    const int rc = noalloc_device(dev, &d);
+    if (rc != PROJ_OK) return rc;
+    int bin = 1;
+    while (bin < B) bin <<= 1;
+    proj_tactic_t t = tp1::choose_tactic(N, K, bin, d->num_cus);
+    while ((t.kernel == PROJ_KERNEL_STREAM || t.kernel == PROJ_KERNEL_STREAM_DOT2) &&
+           t.split < 64 && tp1::stream_lds_bytes(K, t) + tp1::static_lds_bytes(t) > d->lds_limit)
+        ++t.split;
+    if (tp1::tactic_workspace(N, K, t) > kNoallocScratchBytes) return PROJ_ESCRATCH;
+    tp1::LaunchShape sh{N,
+                        K,
+                        B,
+                        static_cast<const uint16_t *>(x),
+                        ldx,
+                        static_cast<const uint16_t *>(W),
+                        static_cast<uint16_t *>(y),
+                        d->scratch,
+                        nullptr,
+                        d->num_cus};
+    const hipError_t e = tp1::launch_projection(sh, t, static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? PROJ_OK : PROJ_EHIP;
 }
 
 int proj_read_probe(const void *buf, size_t bytes, float *sink, int waves_per_cu,

@@ -25,6 +25,10 @@ Default run (prints ONE JSON line):
   TFLOP/s and % of the 2.5 PFLOP/s BF16 MFMA peak for B >= 64.
 * read_ceiling: the library's streaming-read probe over the chain's weights
   back to back and over a 2 GB buffer (the box's plain read rates).
+* prefetch_overlap: the chain with a 10 or 20 us memory-free stand-in for the
+  attention core between each layer's projections, without and with the
+  prefetch of the head (or all) of that layer's o_proj weight on a second
+  stream while the core runs.
 * cpu_baseline: the CPU oracle (FP64 sums) on the same chain, on all host
   cores, over a bounded number of layers; its CPU model; and a one-thread
   figure for the DSA B=1 workload.
@@ -63,6 +67,9 @@ def _args():
                          "'none' skips them")
     ap.add_argument("--headline-only", action="store_true",
                     help="time only the multi-layer stream (e.g. under a profiler)")
+    ap.add_argument("--sweeps-only", action="store_true",
+                    help="time only the per_config workloads and print them as one JSON "
+                         "line (e.g. under a profiler, without the stream's dispatches)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall time of the bounded oracle sample (whole layers)")
@@ -88,10 +95,12 @@ def copy_calibration(torch):
     _say("copy calibration: 5 x 268435456-byte device copies done")
 
 
-def measured_traffic(kernel: str):
-    """HBM bytes per launch of `kernel` from the committed counter summary
-    (profiles/traffic.json), or None when it was taken from another version
-    of the kernel source or never taken."""
+def measured_traffic(kernel: str, B: int, N: int):
+    """HBM bytes per launch of `kernel` (a [B, N] output) from the committed
+    counter summary (profiles/traffic.json), or None when it was taken from
+    another version of the kernel source or never taken.  A split-K call is
+    the main kernel plus the reduction pass, whose entry is keyed by its grid
+    (it serves every shape under one name)."""
     from tp1_skinny_bf16_amd import profile_summary
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
@@ -101,8 +110,13 @@ def measured_traffic(kernel: str):
     if data.get("source_hash") != profile_summary.source_hash():
         return None
     total = 0
-    for part in kernel.split("+"):   # a split-K call is the main kernel + splitk_reduce
-        entry = data.get("kernels", {}).get(part)
+    for part in kernel.split("+"):
+        key = part
+        if part == "splitk_reduce4":
+            key = f"{part}@{-(-B * N // 4 // 256) * 256}"
+        elif part == "splitk_reduce":
+            key = f"{part}@{-(-B * N // 256) * 256}"
+        entry = data.get("kernels", {}).get(key)
         if not entry:
             return None
         total += entry["traffic"]
@@ -202,7 +216,8 @@ def headline(args, torch, tp, wl, timing):
     roof = {"bound": "hbm", "kernel": dom["kernel"], "role": dom_name,
             "achieved": round(achieved, 1), "peak": timing.HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / timing.HBM_PEAK_GBS, 4),
-            "traffic": measured_traffic(dom["kernel"]),
+            "traffic": measured_traffic(dom["kernel"], B,
+                                        wl.DSA_N if dom_name == "in_proj" else wl.OPROJ_N),
             "avg_launch_us": dom["us_per_launch"],
             "bytes_per_launch": dom["bytes_per_launch"]}
 
@@ -220,13 +235,94 @@ def headline(args, torch, tp, wl, timing):
                "in_proj_weight_read_GBps": round(per_launch, 1),
                "sustained_2GB_GBps": round(timing.gbs(big.numel() * 2, rs["us_median"]), 1)}
     del big
+    overlap = overlap_study(torch, wl, timing, stack, x0, y_in, y_o, reps=max(5, args.steps // 2))
     graph = None
     if args.report:
         graph = timing.time_graph([step], replays=10)
     return {"cfg": cfg, "t": t, "value": value, "ms": ms_per_step,
             "gpu_ms": gpu_ms_per_step, "step_bytes": step_bytes, "families": fam,
-            "roofline": roof, "read_ceiling": ceiling, "graph_us": graph,
+            "roofline": roof, "read_ceiling": ceiling, "graph_us": graph, "overlap": overlap,
             "stack": stack, "tensors": (w_in, w_o, x0, y_in, y_o)}
+
+
+def overlap_study(torch, wl, timing, stack, x0, y_in, y_o, reps):
+    """The chain with a memory-free stand-in for the attention core between
+    each layer's projections, without and with the prefetch of the head of
+    that layer's o_proj weight on a second stream during the core (the
+    runtime page's L2 weight prefetch, forked and joined around the core as
+    the hybrid page's NoPrefetch interface does).  us per step."""
+    side = torch.cuda.Stream()               # default priority
+    stream = torch.cuda.current_stream()
+    wo_bytes = wl.OPROJ_N * wl.OPROJ_K * 2
+
+    def timed(core_us, pf):
+        for _ in range(3):
+            stack.run_overlap(x0, y_in, y_o, core_us=core_us, prefetch_bytes=pf,
+                              side_stream=side if pf else None)
+        torch.cuda.synchronize()
+        a, b = _events(torch, 2)
+        a.record(stream)
+        for _ in range(reps):
+            stack.run_overlap(x0, y_in, y_o, core_us=core_us, prefetch_bytes=pf,
+                              side_stream=side if pf else None)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) * 1e3 / reps
+
+    # the most a prefetch can give: o_proj right after its whole weight was
+    # read into the caches, against o_proj cold (the chain's own order)
+    B = x0.shape[0]
+    pin, po = stack.in_plan, stack.out_plan
+    sh = stream.cuda_stream
+
+    def o_proj(l):
+        rc = po.run_ptr(B, y_in[l].data_ptr(), wl.DSA_N, stack.w_o[l].data_ptr(),
+                        y_o[l].data_ptr(), sh)
+        assert rc == 0
+
+    def in_proj(l):
+        x = x0 if l == 0 else y_o[l - 1]
+        rc = pin.run_ptr(B, x.data_ptr(), wl.DSA_K, stack.w_in[l].data_ptr(),
+                         y_in[l].data_ptr(), sh)
+        assert rc == 0
+
+    cold, warm, pf_us = [], [], []
+    from tp1_skinny_bf16_amd import prefetch
+    for rep in range(reps):
+        for l in range(stack.layers):
+            e = _events(torch, 6)
+            in_proj(l)
+            e[0].record(stream)
+            o_proj(l)                                  # cold: straight after in-proj
+            e[1].record(stream)
+            in_proj(l)                                 # evict with the in-proj weight again
+            e[2].record(stream)
+            prefetch(stack.w_o[l], wo_bytes)           # whole o_proj weight
+            e[3].record(stream)
+            o_proj(l)
+            e[4].record(stream)
+            torch.cuda.synchronize()
+            if rep > 0:
+                cold.append(e[0].elapsed_time(e[1]) * 1e3)
+                pf_us.append(e[2].elapsed_time(e[3]) * 1e3)
+                warm.append(e[3].elapsed_time(e[4]) * 1e3)
+    out = {"layers": stack.layers, "o_proj_weight_bytes": wo_bytes,
+           "o_proj_us_cold": round(sum(cold) / len(cold), 2),
+           "o_proj_us_after_full_prefetch": round(sum(warm) / len(warm), 2),
+           "full_prefetch_us": round(sum(pf_us) / len(pf_us), 2),
+           "full_prefetch_GBps": round(timing.gbs(wo_bytes, sum(pf_us) / len(pf_us)), 1),
+           "points": []}
+    for core_us in (10.0, 20.0):
+        base = timed(core_us, 0)
+        row = {"core_us": core_us, "chain_us_no_prefetch": round(base, 1)}
+        # the head the core's duration could fetch at ~6.5 TB/s, and the whole weight
+        for pf in sorted({min(wo_bytes, int(core_us * 6.5e6)) // 16 * 16, wo_bytes}):
+            us = timed(core_us, pf)
+            row[f"chain_us_prefetch_{pf}"] = round(us, 1)
+            row[f"gain_us_prefetch_{pf}"] = round(base - us, 1)
+        out["points"].append(row)
+    _say(f"prefetch beside the core stand-in: {out}")
+    return out
 
 
 def per_config(args, torch, tp, wl, timing, report):
@@ -347,6 +443,12 @@ def main():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
     torch.cuda.set_device(0)
+    if args.sweeps_only:
+        pc = per_config(args, torch, tp, wl, timing, None)
+        if args.copy_calibration:
+            copy_calibration(torch)
+        print(json.dumps({"per_config": pc}), flush=True)
+        return
     _say("timing the 8-layer stream (seed-4 tensors)")
     h = headline(args, torch, tp, wl, timing)
     _say(f"8-layer stream: {h['ms'] * 1e3:.1f} us/step, {h['value']:.1f} GB/s; "
@@ -388,6 +490,7 @@ def main():
         "kernels": h["families"],
         "roofline": h["roofline"],
         "read_ceiling": h["read_ceiling"],
+        "prefetch_overlap": h["overlap"],
         "per_config": pc,
         "cpu_baseline": cpu,
     }

@@ -218,6 +218,43 @@ int proj_run_layers(const proj_plan_t *in, const proj_plan_t *out, int L, int B,
 int proj_run_noalloc(int N, int K, int B, const void *x, long ldx, const void *W, void *y,
                      void *stream);
 
+/*
+ * proj_prefetch -- weight prefetch, the library's counterpart of the "L2
+ * weight prefetch for the specialized decode" the vLLM API page
+ * "vllm.models.kimi_k3.nvidia.specialized_decode.runtime" lists among its
+ * modules.  Enqueue on `stream` a kernel that reads the leading `bytes`
+ * (rounded down to 16) of W with ordinary cached loads, so they sit in the
+ * memory-side cache (MALL) and L2 when a projection streams W next.  It
+ * writes nothing.  Meant for a second stream forked while the GPU's HBM is
+ * otherwise idle (see proj_run_layers_overlap).
+ *   W : device pointer, 16-byte aligned
+ * Returns PROJ_OK, PROJ_EINVAL, PROJ_EALIGN or PROJ_EHIP.
+ */
+int proj_prefetch(const void *W, size_t bytes, void *stream);
+
+/*
+ * proj_run_layers_overlap -- proj_run_layers with the gap between a layer's
+ * two projections filled as a decode step fills it: a stand-in for the
+ * attention core (a kernel of `core_us` microseconds on `stream` that
+ * touches no memory), and, beside it on `side_stream`, the prefetch of the
+ * first `prefetch_bytes` of that layer's o_proj weight.  The fork and join
+ * follow the vLLM API page "vllm.models.kimi_k3.nvidia.specialized_decode.
+ * runtime.hybrid" (section "NoPrefetch": a prefetcher forked before the core
+ * and joined after it): the side stream waits for the input projection,
+ * prefetches, and o_proj waits for the prefetch.  Outputs are those of
+ * proj_run_layers, bit for bit.
+ *   core_us        : 0 .. 1e6 (0 = no stand-in)
+ *   prefetch_bytes : 0 = no prefetch (side_stream unused); capped at the
+ *                    o_proj weight's size
+ *   side_stream    : a second stream of the same priority, not `stream`
+ * Returns as proj_run_layers (PROJ_EINVAL for a bad core_us, or a prefetch
+ * without a distinct side stream).
+ */
+int proj_run_layers_overlap(const proj_plan_t *in, const proj_plan_t *out, int L, int B,
+                            const void *x0, long ldx0, const void *const *W_in,
+                            const void *const *W_o, void *y_in, void *y_o, double core_us,
+                            size_t prefetch_bytes, void *stream, void *side_stream);
+
 /* proj_free -- release a plan and its workspace.  NULL is a no-op. */
 void proj_free(proj_plan_t *plan);
 

@@ -185,6 +185,27 @@ def test_run_layers_argument_checks():
     assert call(pin, po, -1, 64) == tp.PROJ_EINVAL
 
 
+def test_run_layers_overlap_argument_checks():
+    lib = tp.library()
+    pin = tp.Plan(14560, 7168, [64], host_only=True)
+    po = tp.Plan(7168, 12288, [64], host_only=True)
+    W = (ctypes.c_void_p * 2)(0x100000, 0x200000)
+    X, Y1, Y2, S1, S2 = 0x10000000, 0x20000000, 0x30000000, 0x1234, 0x5678
+    call = lambda L, B, core, pf, st, side: lib.proj_run_layers_overlap(  # noqa: E731
+        pin.handle, po.handle, L, B, ctypes.c_void_p(X), 0, W, W, ctypes.c_void_p(Y1),
+        ctypes.c_void_p(Y2), core, pf, ctypes.c_void_p(st), ctypes.c_void_p(side))
+    assert call(2, 64, 5.0, 1 << 20, S1, S2) == tp.PROJ_ENODEV    # host-only plans
+    assert call(2, 64, -1.0, 0, S1, 0) == tp.PROJ_EINVAL          # negative core time
+    assert call(2, 64, float("nan"), 0, S1, 0) == tp.PROJ_EINVAL
+    assert call(2, 64, 5.0, 1 << 20, S1, 0) == tp.PROJ_EINVAL     # prefetch, no side stream
+    assert call(2, 64, 5.0, 1 << 20, S1, S1) == tp.PROJ_EINVAL    # side == main stream
+    assert call(2, 65, 5.0, 0, S1, 0) == tp.PROJ_EBATCH
+    assert call(0, 64, 5.0, 1 << 20, S1, S2) == tp.PROJ_OK        # nothing to do
+    assert lib.proj_prefetch(None, 16, None) == tp.PROJ_EINVAL
+    assert lib.proj_prefetch(ctypes.c_void_p(0x1008), 16, None) == tp.PROJ_EALIGN
+    assert lib.proj_prefetch(ctypes.c_void_p(0x1000), 0, None) == tp.PROJ_OK
+
+
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(bd, "_LIB", None)
     monkeypatch.setattr(bd, "LIB_PATH", str(tmp_path / "absent.so"))

@@ -12,6 +12,6 @@ from ._binding import (EXPORTS, KERNEL_IDS, KERNEL_NAMES,  # noqa: F401
                        KERNEL_STREAM_DOT2,
                        LIB_PATH, MAX_BATCH, MAX_BATCHES, PROJ_EALIGN, PROJ_EBATCH,
                        PROJ_EHIP, PROJ_EINVAL, PROJ_ENODEV, PROJ_ENOMEM, PROJ_ESCRATCH,
-                       PROJ_OK, Plan, ProjError, Tactic, library, read_probe, run_noalloc,
-                       run_noalloc_ptr, strerror)
+                       PROJ_OK, Plan, ProjError, Tactic, library, prefetch, read_probe,
+                       run_noalloc, run_noalloc_ptr, strerror)
 from .layers import LayerStack  # noqa: F401

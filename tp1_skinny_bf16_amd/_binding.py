@@ -40,7 +40,8 @@ MAX_BATCHES = 64
 EXPORTS = ("proj_plan", "proj_run", "proj_free", "proj_strerror",
            "proj_plan_tactic", "proj_plan_set_tactic",
            "proj_plan_workspace_bytes", "proj_read_probe", "proj_run_layers",
-           "proj_plan_kernel_name", "proj_run_noalloc")
+           "proj_plan_kernel_name", "proj_run_noalloc", "proj_prefetch",
+           "proj_run_layers_overlap")
 
 
 class ProjError(RuntimeError):
@@ -120,6 +121,12 @@ def _lib():
     lib.proj_run_layers.argtypes = [vp, vp, ctypes.c_int, ctypes.c_int, vp, ctypes.c_long,
                                     ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp, vp]
     lib.proj_run_layers.restype = ctypes.c_int
+    lib.proj_prefetch.argtypes = [vp, ctypes.c_size_t, vp]
+    lib.proj_prefetch.restype = ctypes.c_int
+    lib.proj_run_layers_overlap.argtypes = [vp, vp, ctypes.c_int, ctypes.c_int, vp, ctypes.c_long,
+                                            ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp,
+                                            ctypes.c_double, ctypes.c_size_t, vp, vp]
+    lib.proj_run_layers_overlap.restype = ctypes.c_int
     lib.proj_run_noalloc.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, vp,
                                      ctypes.c_long, vp, vp, vp]
     lib.proj_run_noalloc.restype = ctypes.c_int
@@ -275,6 +282,13 @@ def run_noalloc(x, W, out, *, stream=None):
                          _stream_handle(stream))
     _check(rc, f"proj_run_noalloc(N={N}, K={K}, B={B})")
     return out
+
+
+def prefetch(W, nbytes: int, stream=None):
+    """Enqueue the prefetch of the leading `nbytes` of weight tensor W."""
+    rc = _lib().proj_prefetch(ctypes.c_void_p(W.data_ptr()), int(nbytes),
+                              ctypes.c_void_p(_stream_handle(stream)))
+    _check(rc, "proj_prefetch")
 
 
 def read_probe(buf, sink, waves_per_cu: int = 0, stream=None):

@@ -852,6 +852,38 @@ __global__ __launch_bounds__(256) void read_probe(const u32x4 *buf, size_t n16,
 }
 
 // ---------------------------------------------------------------------------
+// Weight prefetch: read the leading bytes of a weight with ordinary (cached)
+// 128-bit loads, so that they sit in the memory-side cache (MALL) and L2 when
+// the projection streams them next.  Nothing is written: an empty asm that
+// takes the loaded values keeps the loads alive.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void prefetch_kernel(const u32x4 *buf, size_t n16) {
+    constexpr int U = 8;  // 128 bytes in flight per lane
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += U * stride) {
+        u32x4 v[U];
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            const size_t k = i + j * stride;
+            v[j] = load_cached(reinterpret_cast<const uint16_t *>(buf + (k < n16 ? k : i)));
+        }
+#pragma unroll
+        for (int j = 0; j < U; ++j) asm volatile("" ::"v"(v[j].x));
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Stand-in for the attention core between the two projections of a layer: a
+// kernel of fixed duration that touches no memory (one 64-lane wave per
+// compute unit sleeping on the constant-rate clock), so HBM is idle while it
+// runs.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void core_standin_kernel(unsigned long long ticks) {
+    const unsigned long long t0 = wall_clock64();
+    while (wall_clock64() - t0 < ticks) __builtin_amdgcn_s_sleep(32);
+}
+
+// ---------------------------------------------------------------------------
 // Host-side dispatch.
 // ---------------------------------------------------------------------------
 namespace {
@@ -1062,6 +1094,20 @@ hipError_t allow_dynamic_lds(size_t bytes) {
     TP1_PIPE_INSTANCES(TP1_ALLOW_PIPE)
 #undef TP1_ALLOW_PIPE
     return e;
+}
+
+hipError_t launch_prefetch(const void *buf, size_t bytes, int num_cus, hipStream_t stream) {
+    if (bytes < 16) return hipSuccess;
+    const int blocks = std::max(1, num_cus * 4);
+    hipLaunchKernelGGL(prefetch_kernel, dim3(blocks), dim3(256), 0, stream,
+                       reinterpret_cast<const u32x4 *>(buf), bytes / 16);
+    return hipGetLastError();
+}
+
+hipError_t launch_core_standin(unsigned long long ticks, int num_cus, hipStream_t stream) {
+    hipLaunchKernelGGL(core_standin_kernel, dim3(std::max(1, num_cus)), dim3(64), 0, stream,
+                       ticks);
+    return hipGetLastError();
 }
 
 hipError_t launch_read_probe(const void *buf, size_t bytes, float *sink,

@@ -39,6 +39,15 @@ hipError_t allow_dynamic_lds(size_t bytes);
 // Name of the kernel instance(s) a tactic launches (for profiles).
 int kernel_name(const LaunchShape &sh, const proj_tactic_t &t, char *buf, size_t len);
 
+// Weight prefetch: read the leading `bytes` (rounded down to 16) of buf with
+// cached loads, on 4 workgroups of 256 lanes per compute unit, 128 bytes in
+// flight per lane.
+hipError_t launch_prefetch(const void *buf, size_t bytes, int num_cus, hipStream_t stream);
+
+// Fixed-duration kernel that touches no memory (`ticks` of the constant-rate
+// wall clock), standing in for the attention core between two projections.
+hipError_t launch_core_standin(unsigned long long ticks, int num_cus, hipStream_t stream);
+
 // Streaming-read probe (measurement aid).
 hipError_t launch_read_probe(const void *buf, size_t bytes, float *sink,
                              int waves_per_cu, int num_cus, hipStream_t stream);

@@ -343,6 +343,100 @@ int proj_run_layers(const proj_plan_t *in, const proj_plan_t *out, int L, int B,
     return PROJ_OK;
 }
 
+int proj_prefetch(const void *W, size_t bytes, void *stream) {
+    if (bytes == 0) return PROJ_OK;
+    if (!W) return PROJ_EINVAL;
+    if (!aligned16(W)) return PROJ_EALIGN;
+    int dev = -1, cus = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) {
+        (void)hipGetLastError();
+        return PROJ_EHIP;
+    }
+    return tp1::launch_prefetch(W, bytes, cus, static_cast<hipStream_t>(stream)) == hipSuccess
+               ? PROJ_OK
+               : PROJ_EHIP;
+}
+
+int proj_run_layers_overlap(const proj_plan_t *in, const proj_plan_t *out, int L, int B,
+                            const void *x0, long ldx0, const void *const *W_in,
+                            const void *const *W_o, void *y_in, void *y_o, double core_us,
+                            size_t prefetch_bytes, void *stream, void *side_stream) {
+    if (!in || !out || L < 0 || !W_in || !W_o) return PROJ_EINVAL;
+    if (!(core_us >= 0.0) || core_us > 1.0e6) return PROJ_EINVAL;
+    const tp1::PlanCore &a = in->core;
+    const tp1::PlanCore &b = out->core;
+    if (b.N != a.K || b.K > a.N) return PROJ_EINVAL;
+    if (B < 0 || B > a.batches[a.nb - 1] || B > b.batches[b.nb - 1]) return PROJ_EBATCH;
+    const size_t wo_bytes = (size_t)b.N * b.K * 2u;
+    if (prefetch_bytes > wo_bytes) prefetch_bytes = wo_bytes;
+    if (prefetch_bytes > 0 && (!side_stream || side_stream == stream)) return PROJ_EINVAL;
+    if (L == 0 || B == 0) return PROJ_OK;
+    if (!x0 || !y_in || !y_o) return PROJ_EINVAL;
+    for (int l = 0; l < L; ++l)
+        if (!W_in[l] || !W_o[l]) return PROJ_EINVAL;
+    if (a.flags & PROJ_PLAN_HOST_ONLY || b.flags & PROJ_PLAN_HOST_ONLY) return PROJ_ENODEV;
+    int rate_khz = 0, cus = 0;
+    if (hipDeviceGetAttribute(&rate_khz, hipDeviceAttributeWallClockRate, in->device) !=
+            hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, in->device) !=
+            hipSuccess || rate_khz <= 0) {
+        (void)hipGetLastError();
+        return PROJ_EHIP;
+    }
+    const unsigned long long ticks = (unsigned long long)(core_us * rate_khz / 1000.0 + 0.5);
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipStream_t side = static_cast<hipStream_t>(side_stream);
+    const size_t in_stride = (size_t)B * a.N * 2u;
+    const size_t o_stride = (size_t)B * b.N * 2u;
+    const void *x = x0;
+    long ldx = ldx0;
+    int rc = PROJ_OK;
+    hipEvent_t fork = nullptr, join = nullptr;
+    if (prefetch_bytes > 0 &&
+        (hipEventCreateWithFlags(&fork, hipEventDisableTiming) != hipSuccess ||
+         hipEventCreateWithFlags(&join, hipEventDisableTiming) != hipSuccess)) {
+        (void)hipGetLastError();
+        if (fork) (void)hipEventDestroy(fork);
+        return PROJ_EHIP;
+    }
+    for (int l = 0; l < L && rc == PROJ_OK; ++l) {
+        char *yi = static_cast<char *>(y_in) + l * in_stride;
+        char *yo = static_cast<char *>(y_o) + l * o_stride;
+        rc = proj_run(in, B, x, ldx, W_in[l], yi, stream);
+        if (rc != PROJ_OK) break;
+        if (prefetch_bytes > 0) {
+            // fork: the side stream starts once the input projection is done
+            // (its weight stream no longer competes for HBM) and prefetches
+            // the head of this layer's o_proj weight while the core runs
+            if (hipEventRecord(fork, st) != hipSuccess ||
+                hipStreamWaitEvent(side, fork, 0) != hipSuccess ||
+                tp1::launch_prefetch(W_o[l], prefetch_bytes, cus, side) != hipSuccess ||
+                hipEventRecord(join, side) != hipSuccess) {
+                rc = PROJ_EHIP;
+                break;
+            }
+        }
+        if (ticks > 0 && tp1::launch_core_standin(ticks, cus, st) != hipSuccess) {
+            rc = PROJ_EHIP;
+            break;
+        }
+        // join: o_proj waits for the prefetch
+        if (prefetch_bytes > 0 && hipStreamWaitEvent(st, join, 0) != hipSuccess) {
+            rc = PROJ_EHIP;
+            break;
+        }
+        rc = proj_run(out, B, yi, a.N, W_o[l], yo, stream);
+        x = yo;
+        ldx = b.N;
+    }
+    if (rc == PROJ_EHIP) (void)hipGetLastError();
+    // destroying a recorded event is allowed: it is released once complete
+    if (fork) (void)hipEventDestroy(fork);
+    if (join) (void)hipEventDestroy(join);
+    return rc;
+}
+
 int proj_run_noalloc(int N, int K, int B, const void *x, long ldx, const void *W, void *y,
                      void *stream) {
     // the batch list of the page's "_bins" rule here: powers of two to 256

@@ -61,3 +61,26 @@ class LayerStack:
                                     ctypes.c_void_p(_stream_handle(stream)))
         _check(rc, f"proj_run_layers(L={self.layers}, B={B})")
         return y_in, y_o
+
+    def run_overlap(self, x0, y_in, y_o, *, core_us: float, prefetch_bytes: int = 0,
+                    stream=None, side_stream=None):
+        """The chain with a fixed-duration stand-in for the attention core
+        between each layer's projections and, beside it on `side_stream`,
+        the prefetch of the head of that layer's o_proj weight."""
+        B = x0.shape[0]
+        if tuple(y_in.shape) != (self.layers, B, self.in_plan.N) or not y_in.is_contiguous():
+            raise ValueError("y_in must be contiguous [L, B, N_in]")
+        if tuple(y_o.shape) != (self.layers, B, self.out_plan.N) or not y_o.is_contiguous():
+            raise ValueError("y_o must be contiguous [L, B, N_o]")
+        if x0.stride(1) != 1 or x0.shape[1] != self.in_plan.K:
+            raise ValueError("x0 must be [B, K_in] with unit column stride")
+        ldx = x0.stride(0) if B > 1 else self.in_plan.K
+        side = _stream_handle(side_stream) if side_stream is not None else 0
+        rc = _lib().proj_run_layers_overlap(
+            self.in_plan.handle, self.out_plan.handle, self.layers, B,
+            ctypes.c_void_p(x0.data_ptr()), ldx, self._pin, self._po,
+            ctypes.c_void_p(y_in.data_ptr()), ctypes.c_void_p(y_o.data_ptr()),
+            float(core_us), int(prefetch_bytes), ctypes.c_void_p(_stream_handle(stream)),
+            ctypes.c_void_p(side))
+        _check(rc, f"proj_run_layers_overlap(L={self.layers}, B={B})")
+        return y_in, y_o

@@ -10,7 +10,8 @@ and writes
   <out>/<name>_traffic.md       FETCH_SIZE / WRITE_SIZE per dispatch, scaled by
                                 what the same counter reads for the reference
                                 copy of known size, against algorithmic bytes
-  <out>/traffic.json            per-kernel scaled bytes, tagged with the hash of
+  <out>/traffic.json            per-kernel scaled bytes (by name, and by
+                                name@grid work-items), tagged with the hash of
                                 the kernel source they were taken from
 """
 from __future__ import annotations
@@ -48,10 +49,14 @@ def short(name: str) -> str:
 
 
 def counters(d):
+    """Mean counter value per dispatch, by kernel name and by (name, grid
+    size in work-items): one kernel (the split-K pass) serves several
+    shapes, which only its grid tells apart."""
     rows = list(csv.DictReader(open(_one(os.path.join(d, "**", "*counter_collection.csv")))))
     per = collections.defaultdict(list)
     for r in rows:
         per[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+        per[(r["Kernel_Name"], int(r["Grid_Size"]))].append(float(r["Counter_Value"]))
     return {k: sum(v) / len(v) for k, v in per.items()}, {k: len(v) for k, v in per.items()}
 
 
@@ -67,19 +72,24 @@ def main():
     a = ap.parse_args()
 
     line = json.loads(open(a.bench_json).read().strip().splitlines()[-1])
-    algo = {}  # kernel short name -> algorithmic bytes per launch (mean over its batches)
+    algo = {}  # kernel short name -> algorithmic bytes per launch (mean over its uses)
     from workloads import algorithmic_bytes  # noqa: E402  (repo root on sys.path)
-    cfg = line["config"]
     per_kernel = collections.defaultdict(list)
-    for B, k in line["kernels"].items():
-        per_kernel[k.split("+")[0]].append(algorithmic_bytes(int(B), cfg["N"], cfg["K"]))
+    # the multi-layer stream's two projections (bench.py default / --headline-only)
+    for fam in (line.get("kernels") or {}).values():
+        per_kernel[fam["kernel"].split("+")[0]].append(fam["bytes_per_launch"])
+    # the single-projection workloads (bench.py per_config / --sweeps-only)
+    for cfg in (line.get("per_config") or {}).values():
+        for B, pt in cfg["points"].items():
+            per_kernel[pt["kernel"].split("+")[0]].append(
+                algorithmic_bytes(int(B), cfg["N"], cfg["K"]))
     for k, v in per_kernel.items():
         algo[k] = sum(v) / len(v)
 
     stats = list(csv.DictReader(open(_one(os.path.join(a.kt, "**", "*kernel_stats.csv")))))
     fetch, nf = counters(a.fetch)
     write, nw = counters(a.write)
-    copy_name = next(k for k in fetch if COPY_KERNEL in k)
+    copy_name = next(k for k in fetch if isinstance(k, str) and COPY_KERNEL in k)
     f_scale = fetch[copy_name] * 1024 / COPY_BYTES
     w_scale = write[copy_name] * 1024 / COPY_BYTES
 
@@ -100,21 +110,26 @@ def main():
           f"FETCH_SIZE reads {fetch[copy_name]:.1f} KiB and WRITE_SIZE {write[copy_name]:.1f} KiB, "
           f"so bytes = FETCH_SIZE KiB * 1024 / {f_scale:.5f} and "
           f"WRITE_SIZE KiB * 1024 / {w_scale:.5f}.", "",
-          "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | scaled read MB | scaled write MB "
-          "| algorithmic MB | traffic / algorithmic |",
-          "|---|---|---|---|---|---|---|---|"]
+          "| kernel | grid (work-items) | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB "
+          "| scaled read MB | scaled write MB | algorithmic MB | traffic / algorithmic |",
+          "|---|---|---|---|---|---|---|---|---|"]
     out = {"source_hash": source_hash(), "kernels": {}}
+    grids = collections.Counter(k[0] for k in fetch if not isinstance(k, str))
     for k in fetch:
-        if "tp1::" not in k:
+        name = k if isinstance(k, str) else k[0]
+        if "tp1::" not in name:
             continue
-        s = short(k)
+        s = short(name) if isinstance(k, str) else f"{short(name)}@{k[1]}"
         rd = fetch[k] * 1024 / f_scale
         wr = write.get(k, 0.0) * 1024 / w_scale
-        al = algo.get(s)
-        ratio = f"{(rd + wr) / al:.3f}" if al else "-"
-        tr.append(f"| `{s}` | {nf[k]} | {fetch[k]:.1f} | {write.get(k, 0.0):.1f} | {rd / 1e6:.2f} | "
-                  f"{wr / 1e6:.3f} | {al / 1e6 if al else 0:.2f} | {ratio} |")
         out["kernels"][s] = {"read_bytes": rd, "write_bytes": wr, "traffic": rd + wr}
+        if isinstance(k, str):
+            continue                      # the table lists one row per (kernel, grid)
+        al = algo.get(short(name)) if grids[name] == 1 else None
+        ratio = f"{(rd + wr) / al:.3f}" if al else "-"
+        tr.append(f"| `{short(name)}` | {k[1]} | {nf[k]} | {fetch[k]:.1f} | "
+                  f"{write.get(k, 0.0):.1f} | {rd / 1e6:.2f} | {wr / 1e6:.3f} | "
+                  f"{al / 1e6 if al else 0:.2f} | {ratio} |")
     with open(os.path.join(a.out, f"{a.name}_traffic.md"), "w") as f:
         f.write("\n".join(tr) + "\n")
     path = os.path.join(a.out, "traffic.json")

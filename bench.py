@@ -112,9 +112,9 @@ def measured_traffic(kernel: str, B: int, N: int):
     total = 0
     for part in kernel.split("+"):
         key = part
-        if part == "splitk_reduce4":
+        if part.startswith("splitk_reduce4<"):
             key = f"{part}@{-(-B * N // 4 // 256) * 256}"
-        elif part == "splitk_reduce":
+        elif part.startswith("splitk_reduce<"):
             key = f"{part}@{-(-B * N // 256) * 256}"
         entry = data.get("kernels", {}).get(key)
         if not entry:

@@ -265,19 +265,25 @@ def test_pipe_only_fields_are_validated():
 
 def test_split_reduction_pass_named_by_output_count():
     """A split-K call launches the four-outputs-per-thread reduction when
-    B * N is a multiple of four and the one-per-thread pass otherwise; the
-    kernel name says which (rocprof summaries and traffic figures key on it)."""
+    B * N is a multiple of four and the one-per-thread pass otherwise, each
+    compiled for S = 2..8 slices (<0>: any S); the kernel name says which
+    (rocprof summaries and traffic figures key on it)."""
     t = tp.Tactic(tp.KERNEL_MFMA_PIPE, 16, 2, 4, 1, 1, 128, 4, 1, 4)
     p = tp.Plan(1001, 1024, [16], host_only=True)       # N odd
     p.set_tactic(16, t)
-    assert p.kernel_name(16).endswith("+splitk_reduce4")    # 16 * 1001 % 4 == 0
-    assert p.kernel_name(4).endswith("+splitk_reduce4")
-    assert p.kernel_name(3).endswith("+splitk_reduce")      # 3 * 1001 odd
-    assert not p.kernel_name(3).endswith("4")
+    assert p.kernel_name(16).endswith("+splitk_reduce4<2>")    # 16 * 1001 % 4 == 0
+    assert p.kernel_name(4).endswith("+splitk_reduce4<2>")
+    assert p.kernel_name(3).endswith("+splitk_reduce<2>")      # 3 * 1001 odd
     q = tp.Plan(1002, 1024, [16], host_only=True)
     q.set_tactic(16, t)
-    assert q.kernel_name(2).endswith("+splitk_reduce4")     # 2 * 1002 % 4 == 0
-    assert q.kernel_name(1).endswith("+splitk_reduce")      # 1002 % 4 == 2
+    assert q.kernel_name(2).endswith("+splitk_reduce4<2>")     # 2 * 1002 % 4 == 0
+    assert q.kernel_name(1).endswith("+splitk_reduce<2>")      # 1002 % 4 == 2
+    # slices of 32 (the pipe kernel's K step): 8 of them, then 32
+    q.set_tactic(16, tp.Tactic(tp.KERNEL_MFMA_PIPE, 16, 8, 4, 1, 1, 128, 4, 1, 4))
+    assert q.kernel_name(16).endswith("+splitk_reduce4<8>")
+    s = tp.Plan(1002, 4096, [8], host_only=True)
+    s.set_tactic(8, tp.Tactic(tp.KERNEL_STREAM, 8, 12, 1, 4, 8))
+    assert s.kernel_name(8).endswith("+splitk_reduce4<0>")     # 12 slices
     r = tp.Plan(1001, 1024, [16], host_only=True)
     r.set_tactic(16, tp.Tactic(tp.KERNEL_MFMA_PIPE, 16, 1, 4, 1, 1, 128, 4, 1, 4))
     assert "splitk" not in r.kernel_name(16)                # no split, no pass

@@ -798,30 +798,58 @@ __global__ __launch_bounds__(NWV * 64) void mfma_pipe_kernel(MfmaArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Fixed-order split-K reduction: y[i] = bf16( sum_{s=0}^{S-1} ws[s][i] ).
+// Fixed-order split-K reduction: y[i] = bf16( sum_{s=0}^{S-1} ws[s][i] ),
+// added s = 0..S-1 starting from slice 0's value.  SC > 0: S == SC, all
+// slices loaded before any is added, so the pass costs one memory round
+// trip (a load-add loop waits for each slice in turn); SC == 0: any S, in
+// that loop.
 // ---------------------------------------------------------------------------
+template <int SC>
 __global__ __launch_bounds__(256) void splitk_reduce(const float *ws, uint16_t *y,
                                                      long count, int S) {
     const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= count) return;
-    float acc = ws[i];
-    for (int s = 1; s < S; ++s) acc += ws[(size_t)s * count + i];
+    float acc;
+    if constexpr (SC > 0) {
+        float v[SC];
+#pragma unroll
+        for (int j = 0; j < SC; ++j) v[j] = __builtin_nontemporal_load(ws + (size_t)j * count + i);
+        acc = v[0];
+#pragma unroll
+        for (int j = 1; j < SC; ++j) acc += v[j];
+    } else {
+        acc = ws[i];
+        for (int s = 1; s < S; ++s) acc += ws[(size_t)s * count + i];
+    }
     y[i] = to_bf16(acc);
 }
 
 // The same sum four outputs per thread (count % 4 == 0): one 16-byte load
 // per slice and one 8-byte store, each output still added s = 0..S-1.
+__device__ __forceinline__ void add4(f32x4 &acc, const f32x4 &v) {
+    acc.x += v.x;
+    acc.y += v.y;
+    acc.z += v.z;
+    acc.w += v.w;
+}
+
+template <int SC>
 __global__ __launch_bounds__(256) void splitk_reduce4(const f32x4 *ws, uint2 *y, long count4,
                                                       int S) {
     const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
     if (i >= count4) return;
-    f32x4 acc = __builtin_nontemporal_load(ws + i);
-    for (int s = 1; s < S; ++s) {
-        const f32x4 v = __builtin_nontemporal_load(ws + (size_t)s * count4 + i);
-        acc.x += v.x;
-        acc.y += v.y;
-        acc.z += v.z;
-        acc.w += v.w;
+    f32x4 acc;
+    if constexpr (SC > 0) {
+        f32x4 v[SC];
+#pragma unroll
+        for (int j = 0; j < SC; ++j)
+            v[j] = __builtin_nontemporal_load(ws + (size_t)j * count4 + i);
+        acc = v[0];
+#pragma unroll
+        for (int j = 1; j < SC; ++j) add4(acc, v[j]);
+    } else {
+        acc = __builtin_nontemporal_load(ws + i);
+        for (int s = 1; s < S; ++s) add4(acc, __builtin_nontemporal_load(ws + (size_t)s * count4 + i));
     }
     y[i] = make_uint2((unsigned)to_bf16(acc.x) | ((unsigned)to_bf16(acc.y) << 16),
                       (unsigned)to_bf16(acc.z) | ((unsigned)to_bf16(acc.w) << 16));
@@ -1004,6 +1032,22 @@ hipError_t launch_stream(const LaunchShape &sh, const proj_tactic_t &t,
     return hipErrorInvalidValue;
 }
 
+// The split-K reduction pass of a call with S = SC slices (SC == 0: any S),
+// four outputs per thread when B * N allows it (y is 16-byte aligned:
+// proj_run checks it).
+template <int SC>
+void enqueue_reduce(const LaunchShape &sh, long count, int S, hipStream_t stream) {
+    if (count % 4 == 0) {
+        const long n = count / 4;
+        hipLaunchKernelGGL(splitk_reduce4<SC>, dim3(ceil_div_i(n, 256)), dim3(256), 0, stream,
+                           reinterpret_cast<const f32x4 *>(sh.ws),
+                           reinterpret_cast<uint2 *>(sh.y), n, S);
+    } else {
+        hipLaunchKernelGGL(splitk_reduce<SC>, dim3(ceil_div_i(count, 256)), dim3(256), 0,
+                           stream, sh.ws, sh.y, count, S);
+    }
+}
+
 }  // namespace
 
 hipError_t launch_projection(const LaunchShape &sh, const proj_tactic_t &t,
@@ -1021,13 +1065,16 @@ hipError_t launch_projection(const LaunchShape &sh, const proj_tactic_t &t,
     const int S = slice_count(sh.K, t);
     if (S > 1 && !fused_counters(sh, grid_x(sh, t), S)) {
         const long count = (long)sh.B * sh.N;
-        if (count % 4 == 0)   // y is 16-byte aligned (proj_run checks it)
-            hipLaunchKernelGGL(splitk_reduce4, dim3(ceil_div_i(count / 4, 256)), dim3(256), 0,
-                               stream, reinterpret_cast<const f32x4 *>(sh.ws),
-                               reinterpret_cast<uint2 *>(sh.y), count / 4, S);
-        else
-            hipLaunchKernelGGL(splitk_reduce, dim3(ceil_div_i(count, 256)), dim3(256), 0,
-                               stream, sh.ws, sh.y, count, S);
+        switch (S) {
+            case 2: enqueue_reduce<2>(sh, count, S, stream); break;
+            case 3: enqueue_reduce<3>(sh, count, S, stream); break;
+            case 4: enqueue_reduce<4>(sh, count, S, stream); break;
+            case 5: enqueue_reduce<5>(sh, count, S, stream); break;
+            case 6: enqueue_reduce<6>(sh, count, S, stream); break;
+            case 7: enqueue_reduce<7>(sh, count, S, stream); break;
+            case 8: enqueue_reduce<8>(sh, count, S, stream); break;
+            default: enqueue_reduce<0>(sh, count, S, stream); break;
+        }
         e = hipGetLastError();
     }
     return e;
@@ -1038,7 +1085,9 @@ int kernel_name(const LaunchShape &sh, const proj_tactic_t &t, char *buf, size_t
     const int S = slice_count(sh.K, t);
     const bool split = S > 1 && !fused_counters(sh, grid_x(sh, t), S);
     // the reduction pass launch_projection picks
-    const char *red = ((long)sh.B * sh.N) % 4 == 0 ? "+splitk_reduce4" : "+splitk_reduce";
+    char red[40];
+    snprintf(red, sizeof red, "+splitk_reduce%s<%d>", ((long)sh.B * sh.N) % 4 == 0 ? "4" : "",
+             S >= 2 && S <= 8 ? S : 0);
     int n;
     if (t.kernel == PROJ_KERNEL_STREAM || t.kernel == PROJ_KERNEL_STREAM_DOT2)
         n = snprintf(buf, len, "stream_kernel<%d, %d, %d, %s>%s", t.bcap, t.rows,

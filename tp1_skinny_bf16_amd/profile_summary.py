@@ -89,9 +89,13 @@ def main():
     stats = list(csv.DictReader(open(_one(os.path.join(a.kt, "**", "*kernel_stats.csv")))))
     fetch, nf = counters(a.fetch)
     write, nw = counters(a.write)
-    copy_name = next(k for k in fetch if isinstance(k, str) and COPY_KERNEL in k)
-    f_scale = fetch[copy_name] * 1024 / COPY_BYTES
-    w_scale = write[copy_name] * 1024 / COPY_BYTES
+    # The reference copy's dispatches, told apart by grid from any other
+    # (smaller) device copy the run makes: the copy kernel's grid that
+    # fetches the most per dispatch.
+    copy_key = max((k for k in fetch if not isinstance(k, str) and COPY_KERNEL in k[0]),
+                   key=lambda k: fetch[k])
+    f_scale = fetch[copy_key] * 1024 / COPY_BYTES
+    w_scale = write[copy_key] * 1024 / COPY_BYTES
 
     os.makedirs(a.out, exist_ok=True)
     kt = [f"# Kernel trace: {a.name}", "", "Command:", "", "```", a.command, "```", "",
@@ -107,7 +111,8 @@ def main():
 
     tr = [f"# HBM traffic: {a.name}", "", "Command:", "", "```", a.command, "```", "",
           f"Scale: the reference copy reads and writes {COPY_BYTES} bytes; per dispatch "
-          f"FETCH_SIZE reads {fetch[copy_name]:.1f} KiB and WRITE_SIZE {write[copy_name]:.1f} KiB, "
+          f"(grid {copy_key[1]}, {nf[copy_key]} dispatches) FETCH_SIZE reads "
+          f"{fetch[copy_key]:.1f} KiB and WRITE_SIZE {write[copy_key]:.1f} KiB, "
           f"so bytes = FETCH_SIZE KiB * 1024 / {f_scale:.5f} and "
           f"WRITE_SIZE KiB * 1024 / {w_scale:.5f}.", "",
           "| kernel | grid (work-items) | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB "

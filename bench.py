@@ -25,10 +25,10 @@ Default run (prints ONE JSON line):
   TFLOP/s and % of the 2.5 PFLOP/s BF16 MFMA peak for B >= 64.
 * read_ceiling: the library's streaming-read probe over the chain's weights
   back to back and over a 2 GB buffer (the box's plain read rates).
-* prefetch_overlap: the chain with a 10 or 20 us memory-free stand-in for the
-  attention core between each layer's projections, without and with the
-  prefetch of the head (or all) of that layer's o_proj weight on a second
-  stream while the core runs.
+* prefetch_overlap: the chain with a 10, 20 or 40 us memory-free stand-in for
+  the attention core between each layer's projections, without and with the
+  prefetch of the head (or all) of that layer's o_proj weight while the core
+  runs: on a second stream (fork/join), or inside the stand-in's own launch.
 * cpu_baseline: the CPU oracle (FP64 sums) on the same chain, on all host
   cores, over a bounded number of layers; its CPU model; and a one-thread
   figure for the DSA B=1 workload.
@@ -255,16 +255,16 @@ def overlap_study(torch, wl, timing, stack, x0, y_in, y_o, reps):
     stream = torch.cuda.current_stream()
     wo_bytes = wl.OPROJ_N * wl.OPROJ_K * 2
 
-    def timed(core_us, pf):
+    def timed(core_us, pf, in_core=False):
+        kw = dict(core_us=core_us, prefetch_bytes=pf,
+                  side_stream=side if pf and not in_core else None, prefetch_in_core=in_core)
         for _ in range(3):
-            stack.run_overlap(x0, y_in, y_o, core_us=core_us, prefetch_bytes=pf,
-                              side_stream=side if pf else None)
+            stack.run_overlap(x0, y_in, y_o, **kw)
         torch.cuda.synchronize()
         a, b = _events(torch, 2)
         a.record(stream)
         for _ in range(reps):
-            stack.run_overlap(x0, y_in, y_o, core_us=core_us, prefetch_bytes=pf,
-                              side_stream=side if pf else None)
+            stack.run_overlap(x0, y_in, y_o, **kw)
         b.record(stream)
         torch.cuda.synchronize()
         return a.elapsed_time(b) * 1e3 / reps
@@ -312,14 +312,17 @@ def overlap_study(torch, wl, timing, stack, x0, y_in, y_o, reps):
            "full_prefetch_us": round(sum(pf_us) / len(pf_us), 2),
            "full_prefetch_GBps": round(timing.gbs(wo_bytes, sum(pf_us) / len(pf_us)), 1),
            "points": []}
-    for core_us in (10.0, 20.0):
+    # Per core duration: the chain without prefetch, then with the head the
+    # core's duration could fetch at ~4.5 TB/s (the cached-load rate) and with
+    # the whole weight, each prefetched on a second stream (fork/join) and
+    # inside the stand-in's own launch (no second stream).  us per step.
+    for core_us in (10.0, 20.0, 40.0):
         base = timed(core_us, 0)
-        row = {"core_us": core_us, "chain_us_no_prefetch": round(base, 1)}
-        # the head the core's duration could fetch at ~6.5 TB/s, and the whole weight
-        for pf in sorted({min(wo_bytes, int(core_us * 6.5e6)) // 16 * 16, wo_bytes}):
-            us = timed(core_us, pf)
-            row[f"chain_us_prefetch_{pf}"] = round(us, 1)
-            row[f"gain_us_prefetch_{pf}"] = round(base - us, 1)
+        row = {"core_us": core_us, "chain_us_no_prefetch": round(base, 1),
+               "side_stream": {}, "in_core_launch": {}}
+        for pf in sorted({min(wo_bytes, int(core_us * 4.5e6)) // 16 * 16, wo_bytes}):
+            row["side_stream"][str(pf)] = round(timed(core_us, pf), 1)
+            row["in_core_launch"][str(pf)] = round(timed(core_us, pf, in_core=True), 1)
         out["points"].append(row)
     _say(f"prefetch beside the core stand-in: {out}")
     return out

@@ -246,9 +246,13 @@ int proj_prefetch(const void *W, size_t bytes, void *stream);
  *   core_us        : 0 .. 1e6 (0 = no stand-in)
  *   prefetch_bytes : 0 = no prefetch (side_stream unused); capped at the
  *                    o_proj weight's size
- *   side_stream    : a second stream of the same priority, not `stream`
+ *   side_stream    : a second stream of the same priority; or `stream`
+ *                    itself, and then the prefetch runs inside the
+ *                    stand-in's own launch (one kernel whose other
+ *                    workgroups prefetch while the stand-in sleeps; it lasts
+ *                    as long as the longer of the two), with no fork or join
  * Returns as proj_run_layers (PROJ_EINVAL for a bad core_us, or a prefetch
- * without a distinct side stream).
+ * with a NULL side stream beside a non-NULL `stream`).
  */
 int proj_run_layers_overlap(const proj_plan_t *in, const proj_plan_t *out, int L, int B,
                             const void *x0, long ldx0, const void *const *W_in,

@@ -198,7 +198,10 @@ def test_run_layers_overlap_argument_checks():
     assert call(2, 64, -1.0, 0, S1, 0) == tp.PROJ_EINVAL          # negative core time
     assert call(2, 64, float("nan"), 0, S1, 0) == tp.PROJ_EINVAL
     assert call(2, 64, 5.0, 1 << 20, S1, 0) == tp.PROJ_EINVAL     # prefetch, no side stream
-    assert call(2, 64, 5.0, 1 << 20, S1, S1) == tp.PROJ_EINVAL    # side == main stream
+    # side == main stream: the prefetch runs inside the stand-in's launch (valid;
+    # host-only plans cannot run it)
+    assert call(2, 64, 5.0, 1 << 20, S1, S1) == tp.PROJ_ENODEV
+    assert call(2, 64, 5.0, 1 << 20, 0, 0) == tp.PROJ_ENODEV
     assert call(2, 65, 5.0, 0, S1, 0) == tp.PROJ_EBATCH
     assert call(0, 64, 5.0, 1 << 20, S1, S2) == tp.PROJ_OK        # nothing to do
     assert lib.proj_prefetch(None, 16, None) == tp.PROJ_EINVAL

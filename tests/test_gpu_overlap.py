@@ -6,7 +6,8 @@ lists an L2 weight prefetch among its modules, and the hybrid page's
 attention core and joined after it.  proj_run_layers_overlap puts a
 fixed-duration, memory-free stand-in for the core between each layer's
 input projection and o_proj, and prefetches the head of the o_proj weight
-on a second stream while it runs.  Neither may change a single output bit.
+while it runs: on a second stream, or inside the stand-in's own launch.
+None of it may change a single output bit.
 """
 import numpy as np
 import pytest
@@ -45,16 +46,21 @@ def test_overlap_outputs_equal_the_plain_chain(B):
     torch.cuda.synchronize()
     side = torch.cuda.Stream()              # default priority, like the main stream
     wo_bytes = wl.OPROJ_N * wl.OPROJ_K * 2
-    for core_us, pf in ((0.0, 0), (5.0, 0), (5.0, 64 << 20), (2.0, wo_bytes), (0.0, 1 << 20)):
+    cases = [(0.0, 0, False), (5.0, 0, False), (5.0, 64 << 20, False), (2.0, wo_bytes, False),
+             (0.0, 1 << 20, False), (5.0, 64 << 20, True), (0.0, wo_bytes, True),
+             (3.0, 1000, True)]
+    for core_us, pf, in_core in cases:
         y_in, y_o = stack.buffers(B)
         y_in.fill_(7.0)
         y_o.fill_(7.0)
         stack.run_overlap(x0, y_in, y_o, core_us=core_us, prefetch_bytes=pf,
-                          side_stream=side if pf else None)
+                          side_stream=side if pf and not in_core else None,
+                          prefetch_in_core=in_core)
         torch.cuda.synchronize()
         same = torch.equal(y_in.view(torch.int16), ref_in.view(torch.int16)) and \
             torch.equal(y_o.view(torch.int16), ref_o.view(torch.int16))
-        say(f"B={B} core {core_us} us prefetch {pf} bytes: outputs equal = {same}")
+        say(f"B={B} core {core_us} us prefetch {pf} bytes ({'in the core launch' if in_core else 'side stream'}): "
+            f"outputs equal = {same}")
         assert same
 
 

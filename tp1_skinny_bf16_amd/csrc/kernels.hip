@@ -912,6 +912,40 @@ __global__ __launch_bounds__(64) void core_standin_kernel(unsigned long long tic
 }
 
 // ---------------------------------------------------------------------------
+// The stand-in core and a weight prefetch in one launch: workgroups
+// 0..core_blocks-1 are the stand-in (their first wave sleeps `ticks` of the
+// wall clock, the others leave at once), the rest read the leading bytes of
+// a weight with cached 128-bit loads as prefetch_kernel does.  The launch
+// lasts as long as the longer of the two.  It models a core kernel that
+// issues the next weight's prefetch itself, so no second stream, fork or
+// join is needed.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void core_prefetch_kernel(unsigned long long ticks,
+                                                            const u32x4 *buf, size_t n16,
+                                                            unsigned core_blocks) {
+    if (blockIdx.x < core_blocks) {
+        if (threadIdx.x >= 64) return;
+        const unsigned long long t0 = wall_clock64();
+        while (wall_clock64() - t0 < ticks) __builtin_amdgcn_s_sleep(32);
+        return;
+    }
+    constexpr int U = 8;
+    const size_t nb = gridDim.x - core_blocks;
+    const size_t stride = nb * blockDim.x;
+    for (size_t i = (size_t)(blockIdx.x - core_blocks) * blockDim.x + threadIdx.x; i < n16;
+         i += U * stride) {
+        u32x4 v[U];
+#pragma unroll
+        for (int j = 0; j < U; ++j) {
+            const size_t k = i + j * stride;
+            v[j] = load_cached(reinterpret_cast<const uint16_t *>(buf + (k < n16 ? k : i)));
+        }
+#pragma unroll
+        for (int j = 0; j < U; ++j) asm volatile("" ::"v"(v[j].x));
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Host-side dispatch.
 // ---------------------------------------------------------------------------
 namespace {
@@ -1156,6 +1190,15 @@ hipError_t launch_prefetch(const void *buf, size_t bytes, int num_cus, hipStream
 hipError_t launch_core_standin(unsigned long long ticks, int num_cus, hipStream_t stream) {
     hipLaunchKernelGGL(core_standin_kernel, dim3(std::max(1, num_cus)), dim3(64), 0, stream,
                        ticks);
+    return hipGetLastError();
+}
+
+hipError_t launch_core_prefetch(unsigned long long ticks, const void *buf, size_t bytes,
+                                int num_cus, hipStream_t stream) {
+    const unsigned core = (unsigned)std::max(1, num_cus);
+    const unsigned pf = bytes >= 16 ? core * 4u : 0u;
+    hipLaunchKernelGGL(core_prefetch_kernel, dim3(core + pf), dim3(256), 0, stream, ticks,
+                       reinterpret_cast<const u32x4 *>(buf), bytes / 16, core);
     return hipGetLastError();
 }
 

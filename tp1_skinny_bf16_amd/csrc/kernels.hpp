@@ -48,6 +48,11 @@ hipError_t launch_prefetch(const void *buf, size_t bytes, int num_cus, hipStream
 // wall clock), standing in for the attention core between two projections.
 hipError_t launch_core_standin(unsigned long long ticks, int num_cus, hipStream_t stream);
 
+// The stand-in core (`ticks`, one sleeping wave per compute unit) and the
+// prefetch of the leading `bytes` of buf (as launch_prefetch) in one launch.
+hipError_t launch_core_prefetch(unsigned long long ticks, const void *buf, size_t bytes,
+                                int num_cus, hipStream_t stream);
+
 // Streaming-read probe (measurement aid).
 hipError_t launch_read_probe(const void *buf, size_t bytes, float *sink,
                              int waves_per_cu, int num_cus, hipStream_t stream);

@@ -370,7 +370,9 @@ int proj_run_layers_overlap(const proj_plan_t *in, const proj_plan_t *out, int L
     if (B < 0 || B > a.batches[a.nb - 1] || B > b.batches[b.nb - 1]) return PROJ_EBATCH;
     const size_t wo_bytes = (size_t)b.N * b.K * 2u;
     if (prefetch_bytes > wo_bytes) prefetch_bytes = wo_bytes;
-    if (prefetch_bytes > 0 && (!side_stream || side_stream == stream)) return PROJ_EINVAL;
+    // side_stream == stream: the prefetch runs inside the stand-in's launch
+    const bool in_launch = prefetch_bytes > 0 && side_stream == stream;
+    if (prefetch_bytes > 0 && !in_launch && !side_stream) return PROJ_EINVAL;
     if (L == 0 || B == 0) return PROJ_OK;
     if (!x0 || !y_in || !y_o) return PROJ_EINVAL;
     for (int l = 0; l < L; ++l)
@@ -393,7 +395,8 @@ int proj_run_layers_overlap(const proj_plan_t *in, const proj_plan_t *out, int L
     long ldx = ldx0;
     int rc = PROJ_OK;
     hipEvent_t fork = nullptr, join = nullptr;
-    if (prefetch_bytes > 0 &&
+    const bool forked = prefetch_bytes > 0 && !in_launch;
+    if (forked &&
         (hipEventCreateWithFlags(&fork, hipEventDisableTiming) != hipSuccess ||
          hipEventCreateWithFlags(&join, hipEventDisableTiming) != hipSuccess)) {
         (void)hipGetLastError();
@@ -405,7 +408,14 @@ int proj_run_layers_overlap(const proj_plan_t *in, const proj_plan_t *out, int L
         char *yo = static_cast<char *>(y_o) + l * o_stride;
         rc = proj_run(in, B, x, ldx, W_in[l], yi, stream);
         if (rc != PROJ_OK) break;
-        if (prefetch_bytes > 0) {
+        if (in_launch) {
+            // the stand-in core issues the prefetch itself: one launch on
+            // `stream`, no second stream
+            if (tp1::launch_core_prefetch(ticks, W_o[l], prefetch_bytes, cus, st) != hipSuccess) {
+                rc = PROJ_EHIP;
+                break;
+            }
+        } else if (forked) {
             // fork: the side stream starts once the input projection is done
             // (its weight stream no longer competes for HBM) and prefetches
             // the head of this layer's o_proj weight while the core runs
@@ -417,12 +427,12 @@ int proj_run_layers_overlap(const proj_plan_t *in, const proj_plan_t *out, int L
                 break;
             }
         }
-        if (ticks > 0 && tp1::launch_core_standin(ticks, cus, st) != hipSuccess) {
+        if (!in_launch && ticks > 0 && tp1::launch_core_standin(ticks, cus, st) != hipSuccess) {
             rc = PROJ_EHIP;
             break;
         }
         // join: o_proj waits for the prefetch
-        if (prefetch_bytes > 0 && hipStreamWaitEvent(st, join, 0) != hipSuccess) {
+        if (forked && hipStreamWaitEvent(st, join, 0) != hipSuccess) {
             rc = PROJ_EHIP;
             break;
         }

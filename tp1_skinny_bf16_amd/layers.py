@@ -63,10 +63,11 @@ class LayerStack:
         return y_in, y_o
 
     def run_overlap(self, x0, y_in, y_o, *, core_us: float, prefetch_bytes: int = 0,
-                    stream=None, side_stream=None):
+                    stream=None, side_stream=None, prefetch_in_core: bool = False):
         """The chain with a fixed-duration stand-in for the attention core
-        between each layer's projections and, beside it on `side_stream`,
-        the prefetch of the head of that layer's o_proj weight."""
+        between each layer's projections and the prefetch of the head of
+        that layer's o_proj weight: beside the core on `side_stream`, or,
+        with prefetch_in_core, inside the core's own launch on `stream`."""
         B = x0.shape[0]
         if tuple(y_in.shape) != (self.layers, B, self.in_plan.N) or not y_in.is_contiguous():
             raise ValueError("y_in must be contiguous [L, B, N_in]")
@@ -75,7 +76,10 @@ class LayerStack:
         if x0.stride(1) != 1 or x0.shape[1] != self.in_plan.K:
             raise ValueError("x0 must be [B, K_in] with unit column stride")
         ldx = x0.stride(0) if B > 1 else self.in_plan.K
-        side = _stream_handle(side_stream) if side_stream is not None else 0
+        if prefetch_in_core:
+            side = _stream_handle(stream)
+        else:
+            side = _stream_handle(side_stream) if side_stream is not None else 0
         rc = _lib().proj_run_layers_overlap(
             self.in_plan.handle, self.out_plan.handle, self.layers, B,
             ctypes.c_void_p(x0.data_ptr()), ldx, self._pin, self._po,

@@ -76,8 +76,10 @@ enum proj_kernel {
                                     instead of with a second kernel; both add
                                     the slices in the fixed order s = 0..S-1,
                                     so results are equal bit for bit.  Slower
-                                    on MI355X as measured: each workgroup's
-                                    device-wide release writes its L2 back */
+                                    on MI355X as measured: every workgroup
+                                    waits for its partials to reach the
+                                    device-coherent level before it counts
+                                    in, and the last one reads them all */
 
 /* Limits checked by proj_plan. */
 #define PROJ_MAX_BATCH 256       /* largest batch a plan may list          */

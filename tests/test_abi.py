@@ -308,3 +308,31 @@ def test_noalloc_argument_checks_return_before_any_device_call():
     assert run(100, 64, 2, a + 2, 64, b, c) == tp.PROJ_EALIGN    # misaligned x
     assert run(100, 64, 2, a, 68, b, c) == tp.PROJ_EALIGN        # ldx % 8
     assert run(100, 64, 2, a, 64, b, b + 64) == tp.PROJ_EINVAL   # y overlaps W
+
+
+def test_prefetch_binding_refuses_more_than_the_tensor():
+    """The C ABI cannot see a buffer's extent, so the binding checks it: a
+    prefetch longer than the tensor (or of a negative size) never reaches the
+    library."""
+    import torch
+    W = torch.empty((4, 8), dtype=torch.bfloat16)          # 64 bytes, CPU: never launched
+    with pytest.raises(ValueError):
+        tp.prefetch(W, 65)
+    with pytest.raises(ValueError):
+        tp.prefetch(W, -1)
+    with pytest.raises(ValueError):
+        tp.prefetch(W.t(), 16)
+
+
+def test_bindings_refuse_host_tensors():
+    """The kernels take raw device pointers, so the Python entry points check
+    that every operand is a device tensor before any call into the library."""
+    import torch
+    x = torch.zeros((2, 64), dtype=torch.bfloat16)
+    W = torch.zeros((32, 64), dtype=torch.bfloat16)
+    y = torch.zeros((2, 32), dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        tp.run_noalloc(x, W, y)
+    p = tp.Plan(32, 64, [2], host_only=True)
+    with pytest.raises(ValueError):
+        p.run(x, W, y)

@@ -250,11 +250,21 @@ class Plan:
         if tuple(out.shape) != (B, self.N) or not out.is_contiguous() or \
                 out.dtype != torch.bfloat16:
             raise ValueError("out must be a contiguous bfloat16 [B, N] tensor")
+        _same_device(x, W, out)
         ldx = x.stride(0) if B > 1 else self.K
         rc = self.run_ptr(B, x.data_ptr(), ldx, W.data_ptr(), out.data_ptr(),
                           _stream_handle(stream))
         _check(rc, f"proj_run(B={B})")
         return out
+
+
+def _same_device(*tensors):
+    """Every operand a device tensor on one device (the kernels take raw
+    device pointers: a host tensor's address must never reach them)."""
+    if not all(t.is_cuda for t in tensors):
+        raise ValueError("every operand must be a device tensor")
+    if len({t.device for t in tensors}) != 1:
+        raise ValueError("operands on different devices")
 
 
 def run_noalloc_ptr(N: int, K: int, B: int, x_ptr: int, ldx: int, w_ptr: int, y_ptr: int,
@@ -277,6 +287,7 @@ def run_noalloc(x, W, out, *, stream=None):
         raise ValueError("x must be [B, K] with unit column stride and W contiguous [N, K]")
     if tuple(out.shape) != (B, N) or not out.is_contiguous():
         raise ValueError("out must be a contiguous [B, N] tensor")
+    _same_device(x, W, out)
     ldx = x.stride(0) if B > 1 else K
     rc = run_noalloc_ptr(N, K, B, x.data_ptr(), ldx, W.data_ptr(), out.data_ptr(),
                          _stream_handle(stream))
@@ -285,7 +296,15 @@ def run_noalloc(x, W, out, *, stream=None):
 
 
 def prefetch(W, nbytes: int, stream=None):
-    """Enqueue the prefetch of the leading `nbytes` of weight tensor W."""
+    """Enqueue the prefetch of the leading `nbytes` of weight tensor W (at most
+    its size: the library cannot see the tensor's extent)."""
+    size = W.numel() * W.element_size()
+    if int(nbytes) > 0 and not W.is_cuda:
+        raise ValueError("prefetch needs a device tensor")
+    if not 0 <= int(nbytes) <= size:
+        raise ValueError(f"prefetch of {nbytes} bytes from a {size}-byte tensor")
+    if not W.is_contiguous():
+        raise ValueError("prefetch needs a contiguous tensor")
     rc = _lib().proj_prefetch(ctypes.c_void_p(W.data_ptr()), int(nbytes),
                               ctypes.c_void_p(_stream_handle(stream)))
     _check(rc, "proj_prefetch")

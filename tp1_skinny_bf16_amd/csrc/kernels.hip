@@ -22,6 +22,10 @@
 //                  in the fixed order s = 0..S-1 and rounds to BF16 (no
 //                  atomics, so results are bitwise reproducible);
 //                  splitk_reduce4 does the same four outputs per thread.
+//   prefetch_kernel / core_standin_kernel / core_prefetch_kernel
+//                  the weight prefetch with cached loads, a memory-free
+//                  stand-in for the attention core between two projections,
+//                  and both in one launch.
 //   read_probe     measurement aid: a plain streaming read of a buffer.
 // Every output is rounded once from FP32 to BF16, nearest-even.
 #include "kernels.hpp"

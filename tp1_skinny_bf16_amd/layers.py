@@ -31,6 +31,17 @@ class LayerStack:
         self._pin = (ctypes.c_void_p * max(1, L))(*[w.data_ptr() for w in self.w_in])
         self._po = (ctypes.c_void_p * max(1, L))(*[w.data_ptr() for w in self.w_o])
 
+    def _check_operands(self, x0, y_in, y_o):
+        """bfloat16 device tensors on the weights' device: the library takes
+        raw device pointers, so a host tensor's address must never reach it."""
+        import torch
+        ops = (x0, y_in, y_o)
+        if any(t.dtype != torch.bfloat16 for t in ops):
+            raise TypeError("x0, y_in and y_o must be bfloat16")
+        devs = {t.device for t in ops} | {w.device for w in self.w_in[:1]}
+        if not all(t.is_cuda for t in ops) or len(devs) != 1:
+            raise ValueError("x0, y_in and y_o must be device tensors on the weights' device")
+
     @property
     def layers(self) -> int:
         return len(self.w_in)
@@ -53,6 +64,7 @@ class LayerStack:
             raise ValueError("y_o must be contiguous [L, B, N_o]")
         if x0.stride(1) != 1 or x0.shape[1] != self.in_plan.K:
             raise ValueError("x0 must be [B, K_in] with unit column stride")
+        self._check_operands(x0, y_in, y_o)
         ldx = x0.stride(0) if B > 1 else self.in_plan.K
         rc = _lib().proj_run_layers(self.in_plan.handle, self.out_plan.handle, self.layers,
                                     B, ctypes.c_void_p(x0.data_ptr()), ldx, self._pin,
@@ -75,6 +87,7 @@ class LayerStack:
             raise ValueError("y_o must be contiguous [L, B, N_o]")
         if x0.stride(1) != 1 or x0.shape[1] != self.in_plan.K:
             raise ValueError("x0 must be [B, K_in] with unit column stride")
+        self._check_operands(x0, y_in, y_o)
         ldx = x0.stride(0) if B > 1 else self.in_plan.K
         if prefetch_in_core:
             side = _stream_handle(stream)

@@ -56,14 +56,17 @@ const Entry kTable[] = {
     // projections column-sharded (N/G x 7168), o_proj row-sharded (7168 x
     // 12288/G); up to 64 rotated copies per shard.  Per bin the faster of a
     // full tuning run and a run of bins 32..128 after the single-pass
-    // eight-wave instances were added.
+    // eight-wave instances were added.  After the split-K pass learned to
+    // load every slice before adding, a third full run was checked bin by
+    // bin against the table's tactic in alternating pairs on one box: two
+    // bins changed (1820 x 7168 and 7168 x 3072 at B = 64).
     {1820, 7168, 1, {PROJ_KERNEL_STREAM_DOT2, 1, 1, 2, 4, 4, 0, 0, 0, 0, 0}},  // 8.89 us, 2937.0 GB/s
     {1820, 7168, 2, {PROJ_KERNEL_MFMA_PIPE, 16, 1, 1, 1, 1, 512, 3, 8, 8, 1}},  // 10.06 us, 2597.2 GB/s
     {1820, 7168, 4, {PROJ_KERNEL_MFMA_PIPE, 16, 2, 1, 1, 1, 512, 3, 8, 8, 0}},  // 10.0 us, 2616.3 GB/s
     {1820, 7168, 8, {PROJ_KERNEL_MFMA_PIPE, 16, 2, 1, 1, 1, 256, 4, 8, 8, 1}},  // 10.01 us, 2620.9 GB/s
     {1820, 7168, 16, {PROJ_KERNEL_MFMA_PIPE, 16, 3, 2, 1, 1, 256, 4, 4, 8, 0}},  // 10.48 us, 2517.1 GB/s
     {1820, 7168, 32, {PROJ_KERNEL_MFMA_PIPE, 32, 4, 2, 1, 1, 256, 4, 4, 8, 0}},  // 11.09 us, 2404.6 GB/s
-    {1820, 7168, 64, {PROJ_KERNEL_MFMA_PIPE, 64, 4, 2, 4, 1, 128, 4, 1, 8, 0}},  // 13.73 us, 1984.1 GB/s
+    {1820, 7168, 64, {PROJ_KERNEL_MFMA_PIPE, 64, 8, 4, 2, 1, 128, 4, 1, 8, 0}},  // 12.8 us, 2128.3 GB/s (paired re-check: 13.37 us before)
     {1820, 7168, 128, {PROJ_KERNEL_MFMA_PIPE, 128, 8, 4, 4, 1, 64, 4, 1, 8, 0}},  // 18.01 us, 1576.5 GB/s
     {1820, 7168, 256, {PROJ_KERNEL_MFMA_PIPE, 256, 8, 8, 8, 1, 64, 3, 1, 8, 0}},  // 26.62 us, 1153.0 GB/s
     {3640, 7168, 1, {PROJ_KERNEL_MFMA_PIPE, 16, 1, 1, 1, 1, 512, 4, 8, 8, 0}},  // 10.75 us, 4856.2 GB/s
@@ -99,7 +102,7 @@ const Entry kTable[] = {
     {7168, 3072, 8, {PROJ_KERNEL_MFMA_PIPE, 16, 1, 2, 1, 1, 256, 4, 4, 8, 0}},  // 9.32 us, 4742.9 GB/s
     {7168, 3072, 16, {PROJ_KERNEL_MFMA_PIPE, 16, 1, 2, 1, 1, 256, 4, 4, 8, 0}},  // 9.83 us, 4513.5 GB/s
     {7168, 3072, 32, {PROJ_KERNEL_MFMA_PIPE, 32, 1, 2, 1, 1, 256, 4, 4, 8, 0}},  // 11.69 us, 3823.4 GB/s
-    {7168, 3072, 64, {PROJ_KERNEL_MFMA_PIPE, 64, 1, 2, 2, 1, 128, 4, 2, 8, 0}},  // 14.92 us, 3039.6 GB/s
+    {7168, 3072, 64, {PROJ_KERNEL_MFMA_PIPE, 64, 2, 4, 4, 1, 128, 4, 1, 8, 1}},  // 15.13 us, 2997.4 GB/s (paired re-check: 16.14 us before)
     {7168, 3072, 128, {PROJ_KERNEL_MFMA_PIPE, 128, 2, 4, 4, 1, 64, 4, 1, 8, 1}},  // 20.94 us, 2228.3 GB/s
     {7168, 3072, 256, {PROJ_KERNEL_MFMA_PIPE, 256, 4, 8, 8, 1, 64, 3, 1, 8, 0}},  // 30.39 us, 1621.7 GB/s
     {7168, 6144, 1, {PROJ_KERNEL_MFMA_PIPE, 16, 1, 2, 1, 1, 512, 3, 4, 8, 1}},  // 16.06 us, 5486.1 GB/s

@@ -82,3 +82,28 @@ def test_emit_table_keeps_the_fastest_run_per_bin(tmp_path):
     assert "// 28.0 us" in rows[1]
     md = tune.summarize([str(a), str(b)])
     assert "## 7168 x 12288" in md and "Crossover (first bin whose best tactic is an MFMA kernel): 1" in md
+
+
+def test_recheck_picks_only_bins_whose_choice_beat_the_table_tactic():
+    """The paired re-check looks at a bin only when the run's choice beat the
+    table's own tactic, timed in the same run, by more than the margin;
+    fields missing from older runs read as 0."""
+    table = {(100, 256, 8): tp.Tactic(tp.KERNEL_MFMA_PIPE, 16, 1, 4, 1, 1, 128, 4, 1, 4),
+             (100, 256, 16): tp.Tactic(tp.KERNEL_MFMA_PIPE, 16, 2, 4, 1, 1, 128, 4, 1, 4)}
+    other = tp.Tactic(tp.KERNEL_STREAM, 8, 1, 4, 4, 8)
+
+    def row(t, us):
+        d = t.as_dict()
+        return {"tactic": d, "us": us}
+
+    old_style = table[(100, 256, 16)].as_dict()
+    del old_style["stagger"]                       # an older run without the field
+    run = [{"N": 100, "K": 256, "bins": {
+        "8": {"chosen": row(other, 9.0), "all": [row(other, 9.0), row(table[(100, 256, 8)], 10.0)]},
+        "16": {"chosen": row(table[(100, 256, 16)], 11.0),
+               "all": [{"tactic": old_style, "us": 11.0}]}}}]
+    got = tune.recheck_candidates(run, lambda N, K, b: table[(N, K, b)], 0.015)
+    assert [(N, K, b) for N, K, b, _, _ in got] == [(100, 256, 8)]
+    assert got[0][3] == table[(100, 256, 8)] and got[0][4] == other
+    # within the margin: nothing to re-check
+    assert tune.recheck_candidates(run, lambda N, K, b: table[(N, K, b)], 0.2) == []

@@ -17,6 +17,14 @@ launches (no split-K pass), then the smaller split, then fewer rows per wave.
 The crossover is the smallest batch whose best tactic is an MFMA one.
 
     python -m tp1_skinny_bf16_amd.tune --shape 14560x7168 --bins 1,2,4 --out t.json
+
+A run made on another box than the table's may differ from it by a few
+percent everywhere, so a table change is decided on one box:
+
+    python -m tp1_skinny_bf16_amd.tune --recheck t.json --out r.json
+
+times every bin whose run choice beat the table's tactic (in that run) by more
+than --margin against it again, in --pairs alternating pairs.
 """
 from __future__ import annotations
 
@@ -266,7 +274,88 @@ def summarize(paths) -> str:
     return "\n".join(lines)
 
 
+def _tactic_from(d: dict) -> Tactic:
+    return Tactic(**{**d, "kernel": KERNEL_IDS[d["kernel"]]})
+
+
+def recheck_candidates(run, table_tactic, margin: float):
+    """(N, K, bin, table tactic, run's choice) for every bin of a tuning run
+    whose choice beat the table's tactic, timed in the same run, by more than
+    `margin` (a fraction).  table_tactic(N, K, bin) -> Tactic."""
+    out = []
+    for res in run:
+        for b, r in res["bins"].items():
+            t = table_tactic(res["N"], res["K"], int(b))
+            td = t.as_dict()
+            same = next((row["us"] for row in r["all"]
+                         if {k: row["tactic"].get(k, 0) for k in td} == td), None)
+            best = r["chosen"]
+            if same is not None and best["us"] < same * (1.0 - margin):
+                out.append((res["N"], res["K"], int(b), t, _tactic_from(best["tactic"])))
+    return out
+
+
+def recheck(paths, margin: float = 0.015, pairs: int = 3, reps: int = 60, log=print):
+    """Time each bin's table tactic against a tuning run's choice in
+    alternating pairs on one box, so that box-to-box differences between
+    runs cannot decide the table.  Returns one row per re-checked bin."""
+    run = []
+    for path in paths:
+        with open(path) as f:
+            run += json.load(f)
+
+    def table_tactic(N, K, b):
+        return Plan(N, K, [b], host_only=True).tactic(b)[0]
+
+    cands = recheck_candidates(run, table_tactic, margin)
+    dev = torch.device("cuda:0")
+    rows, shape, copies, x = [], None, None, None
+    for (N, K, b, t_tab, t_new) in cands:
+        if shape != (N, K):
+            copies = None
+            torch.cuda.empty_cache()
+            g = torch.Generator(device=dev)
+            g.manual_seed(7)
+            W0 = (torch.randn((N, K), generator=g, device=dev) * 0.02).to(torch.bfloat16)
+            copies = rotation_copies(W0)
+            x = torch.randn((256, K), generator=g, device=dev).to(torch.bfloat16)
+            shape = (N, K)
+        y = torch.empty((b, N), dtype=torch.bfloat16, device=dev)
+        st = torch.cuda.current_stream().cuda_stream
+        plans = {}
+        for name, t in (("table", t_tab), ("run", t_new)):
+            plans[name] = Plan(N, K, [b])
+            plans[name].set_tactic(b, t)
+        us = {"table": [], "run": []}
+        for _ in range(pairs):
+            for name in ("table", "run"):
+                pl = plans[name]
+                calls = [(lambda W=W, pl=pl: pl.run_ptr(b, x.data_ptr(), K, W.data_ptr(),
+                                                      y.data_ptr(), st)) for W in copies]
+                us[name].append(round(time_calls(calls, warmup=2, reps=reps,
+                                                  warm_seconds=0.1)["us_mean_b2b"], 2))
+        med = {k: sorted(v)[len(v) // 2] for k, v in us.items()}
+        row = {"N": N, "K": K, "bin": b, "table": t_tab.as_dict(), "run": t_new.as_dict(),
+               "table_us": us["table"], "run_us": us["run"],
+               "gain_pct": round(100.0 * (med["table"] - med["run"]) / med["table"], 2)}
+        rows.append(row)
+        if log:
+            log(f"{N}x{K} B={b}: table {us['table']} run {us['run']} -> {row['gain_pct']}%")
+    return rows
+
+
 def main():
+    if len(sys.argv) > 1 and sys.argv[1] == "--recheck":
+        ap = argparse.ArgumentParser(prog="tune --recheck")
+        ap.add_argument("--recheck", nargs="+", required=True, help="tuning run JSON files")
+        ap.add_argument("--margin", type=float, default=0.015)
+        ap.add_argument("--pairs", type=int, default=3)
+        ap.add_argument("--out", required=True)
+        a = ap.parse_args()
+        rows = recheck(a.recheck, a.margin, a.pairs, log=lambda m: print(m, flush=True))
+        with open(a.out, "w") as f:
+            json.dump(rows, f, indent=1)
+        return 0
     if len(sys.argv) > 1 and sys.argv[1] == "--emit-table":
         print(emit_table(sys.argv[2:]))
         return 0

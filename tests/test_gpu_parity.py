@@ -85,6 +85,41 @@ def test_full_config_random(name, B):
     check_random(f"{name} B={B}", y, t["x"][:B], t["W"])        # every output
 
 
+def _structured_inputs(N, K, B, seed):
+    """Inputs unlike the configurations' (every output still gated):
+    x scaled by 1e3 and W by 1e-3 of the usual spread, so products keep their
+    size but every operand sits ~10 binades away; half of x's entries exact
+    zeros; row 0 all +0, row 1 all -0, and row 5 a copy of row 2."""
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    W = wl.normal_bf16((N, K), wl.W_STD * 1e-3, g)
+    x = wl.normal_bf16((B, K), 1e3, g)
+    keep = torch.rand((B, K), generator=g) < 0.5
+    x = torch.where(keep, x, torch.zeros_like(x))
+    x[0] = 0.0
+    x[1] = -0.0
+    x[5] = x[2]
+    return x, W
+
+
+@pytest.mark.parametrize("N,K", [(wl.DSA_N, wl.DSA_K), (wl.OPROJ_N, wl.OPROJ_K),
+                                 (wl.KDA_N, wl.KDA_K)])
+def test_structured_inputs_full_shape(N, K):
+    """Scaled, sparse and degenerate rows at full shape through the planned
+    tactics of B = 8, 16, 64 and 256: every output against the oracle's gates,
+    the zero rows +0 bit for bit (both sides start their sums from +0), and a
+    repeated row repeated bit for bit."""
+    x, W = _structured_inputs(N, K, 256, seed=N + K + 101)
+    assert x[1].view(torch.int16).eq(-32768).all()          # really -0
+    Wd = W.to(DEV)
+    plan = tp.Plan(N, K, BINS)
+    for B in (8, 16, 64, 256):
+        y = gpu_run(plan, x[:B], Wd)
+        check_random(f"structured N={N} K={K} B={B} {tactic_label(plan, B)}", y, x[:B], W)
+        assert (y[0] == 0).all() and (y[1] == 0).all(), "zero rows must give +0"
+        assert np.array_equal(y[2], y[5]), "a repeated row must repeat its outputs"
+
+
 VERIFY_BINS = [3, 6, 12, 24, 48, 96, 192]   # requests x (1 + speculative tokens)
 
 

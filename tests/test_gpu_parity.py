@@ -313,6 +313,27 @@ def test_fused_split_matches_two_pass_bitwise():
             check_random(f"fused split {tactic_label(fused, B)} B={B}", a1, x[:B], W)
 
 
+@pytest.mark.parametrize("N,K", [(wl.DSA_N, wl.DSA_K), (wl.OPROJ_N, wl.OPROJ_K)])
+def test_fused_split_bitwise_at_full_shapes(N, K):
+    """The planned split tactics of B = 64, 128 and 256 at full shape (the
+    8-layer stream uses those of B = 64) under the in-kernel reduction: bit
+    for bit the two-pass result.  Two inputs in turn: a counter left non-zero
+    by one call would send the next call's sum to the wrong workgroup."""
+    bins = [64, 128, 256]
+    x1, W = wl.random_case(256, N, K, seed=31)
+    x2 = wl.random_case(256, N, K, seed=32)[0]
+    Wd = W.to(DEV)
+    fused = tp.Plan(N, K, bins, fused_split=True)
+    twop = tp.Plan(N, K, bins)
+    for B in (64, 128, 256, 61):
+        assert "+splitk_reduce" not in fused.kernel_name(B)
+        for xx in (x1, x2, x1):
+            a = gpu_run(fused, xx[:B], Wd)
+            b = gpu_run(twop, xx[:B], Wd)
+            assert np.array_equal(a, b), f"N={N} B={B}: fused != two-pass"
+        check_random(f"fused split N={N} K={K} B={B} {tactic_label(fused, B)}", a, x1[:B], W)
+
+
 # Per-GPU shards of a G-way tensor-parallel step (the vLLM API page
 # "vllm.models.kimi_k3.nvidia.specialized_decode.runtime.hybrid", section
 # "HybridAttention"): the input projections column-sharded (N/G x K), o_proj

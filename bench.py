@@ -29,6 +29,10 @@ Default run (prints ONE JSON line):
   the attention core between each layer's projections, without and with the
   prefetch of the head (or all) of that layer's o_proj weight while the core
   runs: on a second stream (fork/join), or inside the stand-in's own launch.
+* moe_front: the MoE layer's split-K front, one projection over a packed
+  [part 0 | part 1] weight (proj_pack_rows) against the two parts as separate
+  projections, cold, at K = 7168 and B = 1..64; the pages print neither
+  part's size, so the parts sweep 2048+1024, 4096+2048 and 8192+4096 rows.
 * cpu_baseline: the CPU oracle (FP64 sums) on the same chain, on all host
   cores, over a bounded number of layers; its CPU model; and a one-thread
   figure for the DSA B=1 workload.
@@ -376,6 +380,55 @@ def per_config(args, torch, tp, wl, timing, report):
     return out
 
 
+FRONT_PARTS = ((2048, 1024), (4096, 2048), (8192, 4096))
+FRONT_BATCHES = (1, 4, 16, 64)
+
+
+def moe_front(args, torch, tp, wl, timing):
+    """The MoE front: one projection over the packed [part 0 | part 1] weight
+    against the two parts as separate projections, cold, at K = 7168.  The
+    pages print neither part's size, so the rows sweep (2/3 and 1/3 of N)."""
+    dev = torch.device("cuda:0")
+    K = wl.DSA_K
+    out = {"K": K, "parts_rows": [list(p) for p in FRONT_PARTS], "points": []}
+    for i, (n0, n1) in enumerate(FRONT_PARTS):
+        x, W0 = wl.random_case(max(FRONT_BATCHES), n0, K, seed=40 + i)
+        _, W1 = wl.random_case(1, n1, K, seed=50 + i)
+        x = x.to(dev)
+        packed = tp.pack_rows([W0.to(dev), W1.to(dev)])
+        copies = timing.rotation_copies(packed)
+        N = n0 + n1
+        front = tp.Plan(N, K, list(FRONT_BATCHES))
+        p0, p1 = tp.Plan(n0, K, list(FRONT_BATCHES)), tp.Plan(n1, K, list(FRONT_BATCHES))
+        for B in FRONT_BATCHES:
+            xb = x[:B]
+            y = torch.empty((B, N), dtype=torch.bfloat16, device=dev)
+            y0 = torch.empty((B, n0), dtype=torch.bfloat16, device=dev)
+            y1 = torch.empty((B, n1), dtype=torch.bfloat16, device=dev)
+            one = timing.time_calls([(lambda W=W: front.run(xb, W, y)) for W in copies],
+                                    warmup=3, reps=40)
+
+            def both(W):
+                p0.run(xb, W[:n0], y0)
+                p1.run(xb, W[n0:], y1)
+            two = timing.time_calls([(lambda W=W: both(W)) for W in copies], warmup=3, reps=40)
+            nbytes = wl.algorithmic_bytes(B, N, K)
+            row = {"rows": [n0, n1], "B": B, "front_us_b2b": round(one["us_mean_b2b"], 2),
+                   "separate_us_b2b": round(two["us_mean_b2b"], 2),
+                   "front_GBps_b2b": round(timing.gbs(nbytes, one["us_mean_b2b"]), 1),
+                   "front_pct_peak_b2b": round(100 * timing.gbs(nbytes, one["us_mean_b2b"])
+                                               / timing.HBM_PEAK_GBS, 1),
+                   "kernel": front.kernel_name(B)}
+            out["points"].append(row)
+            _say(f"moe front {n0}+{n1} B={B:2d}: one launch {row['front_us_b2b']:6.2f} us "
+                 f"({row['front_pct_peak_b2b']:4.1f}%), two launches {row['separate_us_b2b']:6.2f} us")
+        for pl in (front, p0, p1):
+            pl.close()
+        del copies, packed
+        torch.cuda.empty_cache()
+    return out
+
+
 def _cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -460,6 +513,9 @@ def main():
     pc = None
     if not args.headline_only and args.configs != "none":
         pc = per_config(args, torch, tp, wl, timing, report)
+    front = None
+    if not args.headline_only and args.configs != "none":
+        front = moe_front(args, torch, tp, wl, timing)
     cpu = None
     if not args.no_cpu and not args.headline_only:
         _say("timing the CPU oracle")
@@ -495,6 +551,7 @@ def main():
         "read_ceiling": h["read_ceiling"],
         "prefetch_overlap": h["overlap"],
         "per_config": pc,
+        "moe_front": front,
         "cpu_baseline": cpu,
     }
     if args.report:

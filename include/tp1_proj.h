@@ -81,14 +81,16 @@ enum proj_kernel {
                                     device-coherent level before it counts
                                     in, and the last one reads them all */
 
-/* Limits checked by proj_plan. */
+/* Limits checked by proj_plan (and proj_pack_rows). */
 #define PROJ_MAX_BATCH 256       /* largest batch a plan may list          */
 #define PROJ_MAX_BATCHES 64      /* longest batch list                     */
+#define PROJ_MAX_PACK 64         /* most weights proj_pack_rows stacks     */
 
 /*
  * A tactic: how one batch bin runs.  Filled in from the library's measured
- * table (or its default rule for shapes it has not measured), or set with
- * proj_plan_set_tactic.
+ * table; for a shape it has not measured, from the nearest measured shape
+ * within a factor of two (|ln(N/N')| + |ln(K/K')| <= ln 2) whose tactic is
+ * valid for it, else from a default rule; or set with proj_plan_set_tactic.
  *   kernel : enum proj_kernel
  *   bcap   : batch capacity of the kernel instance (>= the bin)
  *   split  : number of K slices S; S > 1 adds a fixed-order reduction pass
@@ -204,7 +206,7 @@ int proj_run_layers(const proj_plan_t *in, const proj_plan_t *out, int L, int B,
  *   N, K, x, ldx, W, y, stream : as for proj_plan / proj_run
  *   B      : 0 <= B <= 256; the tactic is the one a plan for the batches
  *            1, 2, 4, ..., 256 would use for B (the smallest power of two
- *            >= B), taken from the same measured table and default rule
+ *            >= B), chosen by the same measured table and rules
  * Split-K partial sums go to a fixed 32 MiB device array of the library
  * (one per GPU, held until the process ends) instead of a plan's workspace;
  * nothing in it needs to start at zero, since every partial is written
@@ -219,6 +221,31 @@ int proj_run_layers(const proj_plan_t *in, const proj_plan_t *out, int L, int B,
  */
 int proj_run_noalloc(int N, int K, int B, const void *x, long ldx, const void *W, void *y,
                      void *stream);
+
+/*
+ * proj_pack_rows -- stack the rows of n weights into one weight, as the MoE
+ * layer's split-K front packs the shared expert's gate_up rows and the
+ * latent down-projection rows into one [shared gate_up | latent down] weight
+ * (vLLM API page "vllm.models.kimi_k3.nvidia.specialized_decode.runtime.dep":
+ * its opening text and section "DepMoe", whose front weight is the packed
+ * one), so that a single projection launch computes every part:
+ *     dst[r0_i + r, :] = src_i[r, :],  r0_i = rows[0] + ... + rows[i-1].
+ * With a plan for the packed [sum(rows), K] weight, proj_run's output
+ * columns [r0_i, r0_i + rows[i]) are x . src_i^T.
+ *   dst    : BF16 [sum(rows), K] device buffer, contiguous, 16-byte aligned
+ *   src    : host array of n device pointers to BF16 [rows[i], K],
+ *            contiguous, 16-byte aligned; none may overlap dst
+ *   rows   : host array of n row counts, each >= 1
+ *   n      : 1..PROJ_MAX_PACK
+ *   K      : row length in elements, K > 0, K % 8 == 0
+ *   stream : a hipStream_t (NULL = the default stream)
+ * Enqueues n device-to-device copies on `stream` (weight preparation, done
+ * once; not part of a projection call) and returns without waiting.
+ * Returns PROJ_OK, PROJ_EINVAL, PROJ_EALIGN or PROJ_EHIP; on an argument
+ * error nothing is enqueued.
+ */
+int proj_pack_rows(void *dst, const void *const *src, const int *rows, int n, int K,
+                   void *stream);
 
 /*
  * proj_prefetch -- weight prefetch, the library's counterpart of the "L2

@@ -336,3 +336,44 @@ def test_bindings_refuse_host_tensors():
     p = tp.Plan(32, 64, [2], host_only=True)
     with pytest.raises(ValueError):
         p.run(x, W, y)
+
+
+def test_pack_rows_argument_checks_on_the_host():
+    # every case is refused before any HIP call: the pointers are never used
+    st = 0
+    good_dst, good_src = 0x100000, 0x400000
+    assert tp.pack_rows_ptr(0, [good_src], [4], 64, st) == tp.PROJ_EINVAL          # no dst
+    assert tp.pack_rows_ptr(good_dst, [], [], 64, st) == tp.PROJ_EINVAL           # n = 0
+    assert tp.pack_rows_ptr(good_dst, [good_src] * (tp.MAX_PACK + 1),
+                            [1] * (tp.MAX_PACK + 1), 64, st) == tp.PROJ_EINVAL    # n too large
+    assert tp.pack_rows_ptr(good_dst, [good_src], [4], 60, st) == tp.PROJ_EINVAL  # K % 8
+    assert tp.pack_rows_ptr(good_dst, [good_src], [4], 0, st) == tp.PROJ_EINVAL   # K = 0
+    assert tp.pack_rows_ptr(good_dst, [good_src], [0], 64, st) == tp.PROJ_EINVAL  # empty part
+    assert tp.pack_rows_ptr(good_dst, [0], [4], 64, st) == tp.PROJ_EINVAL         # no source
+    assert tp.pack_rows_ptr(good_dst + 8, [good_src], [4], 64, st) == tp.PROJ_EALIGN
+    assert tp.pack_rows_ptr(good_dst, [good_src + 8], [4], 64, st) == tp.PROJ_EALIGN
+    # a source inside the destination's 2 x 4 x 64 x 2 = 1 KiB, or the other way round
+    assert tp.pack_rows_ptr(good_dst, [good_src, good_dst + 512], [4, 4], 64, st) == tp.PROJ_EINVAL
+    assert tp.pack_rows_ptr(good_dst, [good_dst - 256], [4], 64, st) == tp.PROJ_EINVAL
+
+
+def test_unmeasured_shape_takes_the_nearest_measured_tactic():
+    # 3072 x 7168 is within a factor of two of the measured 3640 x 7168 (and
+    # nearer to it than to 1820 or 6172 rows): it takes that shape's tactic at
+    # every bin where the tactic is valid for it
+    bins = [1, 2, 4, 8, 16, 32, 64, 128, 256]
+    near = tp.Plan(3072, 7168, bins, host_only=True)
+    ref = tp.Plan(3640, 7168, bins, host_only=True)
+    for b in bins:
+        assert near.tactic(b)[0] == ref.tactic(b)[0], b
+    # an in-between bin takes the neighbour's tactic for the next measured bin
+    mid = tp.Plan(3072, 7168, [3, 12, 100], host_only=True)
+    for b, up in ((3, 4), (12, 16), (100, 128)):
+        assert mid.tactic(b)[0] == ref.tactic(up)[0], b
+    # nothing measured within a factor of two: the default rule (the weight
+    # stream for one row, the pipelined kernel above)
+    far = tp.Plan(1000, 1032, bins, host_only=True)
+    assert far.tactic(1)[0].kernel == tp.KERNEL_STREAM
+    assert far.tactic(64)[0].kernel == tp.KERNEL_MFMA_PIPE
+    # the measured shapes themselves are unchanged
+    assert ref.tactic(1)[0] != far.tactic(1)[0]

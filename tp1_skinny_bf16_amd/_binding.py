@@ -35,13 +35,14 @@ PLAN_HOST_ONLY = 0x1
 PLAN_SPLIT_FUSED = 0x2
 MAX_BATCH = 256
 MAX_BATCHES = 64
+MAX_PACK = 64
 
 # every symbol include/tp1_proj.h declares
 EXPORTS = ("proj_plan", "proj_run", "proj_free", "proj_strerror",
            "proj_plan_tactic", "proj_plan_set_tactic",
            "proj_plan_workspace_bytes", "proj_read_probe", "proj_run_layers",
            "proj_plan_kernel_name", "proj_run_noalloc", "proj_prefetch",
-           "proj_run_layers_overlap")
+           "proj_run_layers_overlap", "proj_pack_rows")
 
 
 class ProjError(RuntimeError):
@@ -123,6 +124,9 @@ def _lib():
     lib.proj_run_layers.restype = ctypes.c_int
     lib.proj_prefetch.argtypes = [vp, ctypes.c_size_t, vp]
     lib.proj_prefetch.restype = ctypes.c_int
+    lib.proj_pack_rows.argtypes = [vp, ctypes.POINTER(vp), ctypes.POINTER(ctypes.c_int),
+                                   ctypes.c_int, ctypes.c_int, vp]
+    lib.proj_pack_rows.restype = ctypes.c_int
     lib.proj_run_layers_overlap.argtypes = [vp, vp, ctypes.c_int, ctypes.c_int, vp, ctypes.c_long,
                                             ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp,
                                             ctypes.c_double, ctypes.c_size_t, vp, vp]
@@ -308,6 +312,39 @@ def prefetch(W, nbytes: int, stream=None):
     rc = _lib().proj_prefetch(ctypes.c_void_p(W.data_ptr()), int(nbytes),
                               ctypes.c_void_p(_stream_handle(stream)))
     _check(rc, "proj_prefetch")
+
+
+def pack_rows_ptr(dst: int, srcs, rows, K: int, stream: int = 0) -> int:
+    """proj_pack_rows on raw device pointers; returns the status code."""
+    n = len(srcs)
+    src_arr = (ctypes.c_void_p * max(1, n))(*[int(p) for p in srcs])
+    row_arr = (ctypes.c_int * max(1, n))(*[int(r) for r in rows])
+    return _lib().proj_pack_rows(ctypes.c_void_p(int(dst)), src_arr, row_arr, n, int(K),
+                                 ctypes.c_void_p(int(stream)))
+
+
+def pack_rows(weights, out=None, stream=None):
+    """Stack BF16 [rows_i, K] device tensors into one [sum(rows_i), K] weight
+    (allocated unless `out` is given) with proj_pack_rows; returns it."""
+    import torch
+    weights = list(weights)
+    if not weights:
+        raise ValueError("nothing to pack")
+    K = weights[0].shape[1]
+    for w in weights:
+        if w.dtype != torch.bfloat16 or w.dim() != 2 or w.shape[1] != K:
+            raise ValueError("weights must be 2-D bfloat16 tensors with one row length")
+        if not w.is_contiguous():
+            raise ValueError("weights must be contiguous")
+    rows = [w.shape[0] for w in weights]
+    if out is None:
+        out = torch.empty((sum(rows), K), dtype=torch.bfloat16, device=weights[0].device)
+    if out.dtype != torch.bfloat16 or tuple(out.shape) != (sum(rows), K) or not out.is_contiguous():
+        raise ValueError(f"out must be a contiguous bfloat16 [{sum(rows)}, {K}] tensor")
+    _same_device(out, *weights)
+    _check(pack_rows_ptr(out.data_ptr(), [w.data_ptr() for w in weights], rows, K,
+                         _stream_handle(stream)), "proj_pack_rows")
+    return out
 
 
 def read_probe(buf, sink, waves_per_cu: int = 0, stream=None):

@@ -196,6 +196,14 @@ proj_tactic_t choose_tactic(int N, int K, int bin, int num_cus) {
     proj_tactic_t t;
     if (lookup_measured_tactic(N, K, bin, &t) && check_tactic(N, K, bin, t) == PROJ_OK)
         return t;
+    // A shape the table has not measured takes the tactic measured for the
+    // nearest shape within a factor of two, if it is valid here: a tactic
+    // fixes how a row range and a K slice are walked, which carries over
+    // between similar shapes better than the default rule does.
+    proj_tactic_t near[8];
+    const int n = nearby_measured_tactics(N, K, bin, near, 8);
+    for (int i = 0; i < n; ++i)
+        if (check_tactic(N, K, bin, near[i]) == PROJ_OK) return near[i];
     return default_tactic(N, K, bin, num_cus);
 }
 

@@ -496,6 +496,38 @@ int proj_run_noalloc(int N, int K, int B, const void *x, long ldx, const void *W
     return e == hipSuccess ? PROJ_OK : PROJ_EHIP;
 }
 
+int proj_pack_rows(void *dst, const void *const *src, const int *rows, int n, int K,
+                   void *stream) {
+    if (!dst || !src || !rows || n < 1 || n > PROJ_MAX_PACK || K <= 0 || (K % 8) != 0)
+        return PROJ_EINVAL;
+    if (!aligned16(dst)) return PROJ_EALIGN;
+    const size_t row_bytes = (size_t)K * 2u;
+    size_t total = 0;
+    for (int i = 0; i < n; ++i) {
+        if (!src[i] || rows[i] < 1) return PROJ_EINVAL;
+        if (!aligned16(src[i])) return PROJ_EALIGN;
+        total += (size_t)rows[i] * row_bytes;
+    }
+    // no source may overlap the destination (the copies would read what
+    // they have already written)
+    const uintptr_t d0 = (uintptr_t)dst, d1 = d0 + total;
+    for (int i = 0; i < n; ++i) {
+        const uintptr_t s0 = (uintptr_t)src[i], s1 = s0 + (size_t)rows[i] * row_bytes;
+        if (s0 < d1 && d0 < s1) return PROJ_EINVAL;
+    }
+    const hipStream_t st = static_cast<hipStream_t>(stream);
+    char *out = static_cast<char *>(dst);
+    for (int i = 0; i < n; ++i) {
+        const size_t bytes = (size_t)rows[i] * row_bytes;
+        if (hipMemcpyAsync(out, src[i], bytes, hipMemcpyDeviceToDevice, st) != hipSuccess) {
+            (void)hipGetLastError();
+            return PROJ_EHIP;
+        }
+        out += bytes;
+    }
+    return PROJ_OK;
+}
+
 int proj_read_probe(const void *buf, size_t bytes, float *sink, int waves_per_cu,
                     void *stream) {
     if (!buf || !sink || bytes == 0 || (bytes % 16) != 0) return PROJ_EINVAL;

@@ -7,6 +7,9 @@
 // Rows: {N, K, bin, {kernel, bcap, split, rows, waves, wpc, kc, depth, kw, nw, stagger}}.
 #include "tactics_table.hpp"
 
+#include <algorithm>
+#include <cmath>
+
 namespace tp1 {
 
 namespace {
@@ -158,6 +161,36 @@ bool lookup_measured_tactic(int N, int K, int bin, proj_tactic_t *out) {
     if (!best) return false;
     *out = best->t;
     return true;
+}
+
+int nearby_measured_tactics(int N, int K, int bin, proj_tactic_t *out, int max_out) {
+    // Shapes measured with a bin at or above `bin`, by distance
+    // |ln(N/N')| + |ln(K/K')|, keeping those within ln 2; each gives the
+    // tactic of its smallest such bin.
+    struct Cand {
+        double d;
+        const Entry *e;
+    };
+    Cand c[sizeof kTable / sizeof kTable[0]];
+    int n = 0;
+    for (const Entry &e : kTable) {
+        if (e.bin < bin || e.t.kernel == 0 || (e.N == N && e.K == K)) continue;
+        const double d = std::fabs(std::log((double)N / e.N)) + std::fabs(std::log((double)K / e.K));
+        if (d > std::log(2.0)) continue;
+        int j = 0;
+        while (j < n && !(c[j].e->N == e.N && c[j].e->K == e.K)) ++j;
+        if (j < n) {
+            if (e.bin < c[j].e->bin) c[j].e = &e;  // the smallest bin >= `bin`
+            continue;
+        }
+        c[n++] = Cand{d, &e};
+    }
+    std::sort(c, c + n, [](const Cand &a, const Cand &b) {
+        return a.d < b.d || (a.d == b.d && (a.e->N < b.e->N || (a.e->N == b.e->N && a.e->K < b.e->K)));
+    });
+    const int m = std::min(n, max_out);
+    for (int i = 0; i < m; ++i) out[i] = c[i].e->t;
+    return m;
 }
 
 }  // namespace tp1

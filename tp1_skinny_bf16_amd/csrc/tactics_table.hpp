@@ -10,4 +10,10 @@ namespace tp1 {
 // measured or every measured bin is below `bin`.
 bool lookup_measured_tactic(int N, int K, int bin, proj_tactic_t *out);
 
+// For a shape the table has not measured: the tactics of measured shapes
+// within a factor of two (|ln(N/N')| + |ln(K/K')| <= ln 2), nearest first,
+// each that shape's tactic for the smallest measured bin >= bin; at most
+// max_out of them.  Returns how many were written.
+int nearby_measured_tactics(int N, int K, int bin, proj_tactic_t *out, int max_out);
+
 }  // namespace tp1

@@ -74,6 +74,15 @@ def _args():
     ap.add_argument("--sweeps-only", action="store_true",
                     help="time only the per_config workloads and print them as one JSON "
                          "line (e.g. under a profiler, without the stream's dispatches)")
+    ap.add_argument("--front-only", action="store_true",
+                    help="time only the MoE front study and print it as one JSON line")
+    ap.add_argument("--front-reps", type=int, default=40,
+                    help="timed rounds per MoE front point (fewer under a profiler)")
+    ap.add_argument("--front-sizes", default=None,
+                    help="comma-separated indices of the MoE front sizes to time (default: all)")
+    ap.add_argument("--front-no-separate", action="store_true",
+                    help="skip the separate-launch comparison (a profile then holds only "
+                         "front launches)")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall time of the bounded oracle sample (whole layers)")
@@ -390,8 +399,11 @@ def moe_front(args, torch, tp, wl, timing):
     pages print neither part's size, so the rows sweep (2/3 and 1/3 of N)."""
     dev = torch.device("cuda:0")
     K = wl.DSA_K
-    out = {"K": K, "parts_rows": [list(p) for p in FRONT_PARTS], "points": []}
-    for i, (n0, n1) in enumerate(FRONT_PARTS):
+    sizes = range(len(FRONT_PARTS)) if args.front_sizes is None else \
+        [int(v) for v in args.front_sizes.split(",")]
+    out = {"K": K, "parts_rows": [list(FRONT_PARTS[i]) for i in sizes], "points": []}
+    for i in sizes:
+        n0, n1 = FRONT_PARTS[i]
         x, W0 = wl.random_case(max(FRONT_BATCHES), n0, K, seed=40 + i)
         _, W1 = wl.random_case(1, n1, K, seed=50 + i)
         x = x.to(dev)
@@ -406,22 +418,24 @@ def moe_front(args, torch, tp, wl, timing):
             y0 = torch.empty((B, n0), dtype=torch.bfloat16, device=dev)
             y1 = torch.empty((B, n1), dtype=torch.bfloat16, device=dev)
             one = timing.time_calls([(lambda W=W: front.run(xb, W, y)) for W in copies],
-                                    warmup=3, reps=40)
+                                    warmup=3, reps=args.front_reps)
 
             def both(W):
                 p0.run(xb, W[:n0], y0)
                 p1.run(xb, W[n0:], y1)
-            two = timing.time_calls([(lambda W=W: both(W)) for W in copies], warmup=3, reps=40)
+            two = None if args.front_no_separate else timing.time_calls(
+                [(lambda W=W: both(W)) for W in copies], warmup=3, reps=args.front_reps)
             nbytes = wl.algorithmic_bytes(B, N, K)
-            row = {"rows": [n0, n1], "B": B, "front_us_b2b": round(one["us_mean_b2b"], 2),
-                   "separate_us_b2b": round(two["us_mean_b2b"], 2),
+            row = {"rows": [n0, n1], "N": N, "K": K, "B": B,
+                   "front_us_b2b": round(one["us_mean_b2b"], 2),
+                   "separate_us_b2b": round(two["us_mean_b2b"], 2) if two else None,
                    "front_GBps_b2b": round(timing.gbs(nbytes, one["us_mean_b2b"]), 1),
                    "front_pct_peak_b2b": round(100 * timing.gbs(nbytes, one["us_mean_b2b"])
                                                / timing.HBM_PEAK_GBS, 1),
                    "kernel": front.kernel_name(B)}
             out["points"].append(row)
             _say(f"moe front {n0}+{n1} B={B:2d}: one launch {row['front_us_b2b']:6.2f} us "
-                 f"({row['front_pct_peak_b2b']:4.1f}%), two launches {row['separate_us_b2b']:6.2f} us")
+                 f"({row['front_pct_peak_b2b']:4.1f}%), two launches {row['separate_us_b2b']} us")
         for pl in (front, p0, p1):
             pl.close()
         del copies, packed
@@ -499,6 +513,12 @@ def main():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
     torch.cuda.set_device(0)
+    if args.front_only:
+        front = moe_front(args, torch, tp, wl, timing)
+        if args.copy_calibration:
+            copy_calibration(torch)
+        print(json.dumps({"moe_front": front}), flush=True)
+        return
     if args.sweeps_only:
         pc = per_config(args, torch, tp, wl, timing, None)
         if args.copy_calibration:

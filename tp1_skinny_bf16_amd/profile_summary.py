@@ -49,15 +49,16 @@ def short(name: str) -> str:
 
 
 def counters(d):
-    """Mean counter value per dispatch, by kernel name and by (name, grid
-    size in work-items): one kernel (the split-K pass) serves several
-    shapes, which only its grid tells apart."""
+    """Mean and largest counter value per dispatch, by kernel name and by
+    (name, grid size in work-items): one kernel (the split-K pass) serves
+    several shapes, which only its grid tells apart."""
     rows = list(csv.DictReader(open(_one(os.path.join(d, "**", "*counter_collection.csv")))))
     per = collections.defaultdict(list)
     for r in rows:
         per[r["Kernel_Name"]].append(float(r["Counter_Value"]))
         per[(r["Kernel_Name"], int(r["Grid_Size"]))].append(float(r["Counter_Value"]))
-    return {k: sum(v) / len(v) for k, v in per.items()}, {k: len(v) for k, v in per.items()}
+    return ({k: sum(v) / len(v) for k, v in per.items()}, {k: len(v) for k, v in per.items()},
+            {k: max(v) for k, v in per.items()})
 
 
 def main():
@@ -83,19 +84,24 @@ def main():
         for B, pt in cfg["points"].items():
             per_kernel[pt["kernel"].split("+")[0]].append(
                 algorithmic_bytes(int(B), cfg["N"], cfg["K"]))
+    # the MoE front's one-launch calls (bench.py moe_front / --front-only)
+    for pt in ((line.get("moe_front") or {}).get("points") or []):
+        per_kernel[pt["kernel"].split("+")[0]].append(algorithmic_bytes(pt["B"], pt["N"], pt["K"]))
     for k, v in per_kernel.items():
         algo[k] = sum(v) / len(v)
 
     stats = list(csv.DictReader(open(_one(os.path.join(a.kt, "**", "*kernel_stats.csv")))))
-    fetch, nf = counters(a.fetch)
-    write, nw = counters(a.write)
-    # The reference copy's dispatches, told apart by grid from any other
-    # (smaller) device copy the run makes: the copy kernel's grid that
-    # fetches the most per dispatch.
+    fetch, nf, fmax = counters(a.fetch)
+    write, nw, wmax = counters(a.write)
+    # The reference copy: the copy kernel's dispatches that fetch the most.
+    # Any other device copy of the run (a smaller one, possibly with the same
+    # grid, such as the packing of a weight) fetches less, so the largest
+    # value per dispatch is the reference's.
     copy_key = max((k for k in fetch if not isinstance(k, str) and COPY_KERNEL in k[0]),
-                   key=lambda k: fetch[k])
-    f_scale = fetch[copy_key] * 1024 / COPY_BYTES
-    w_scale = write[copy_key] * 1024 / COPY_BYTES
+                   key=lambda k: fmax[k])
+    copy_fetch, copy_write = fmax[copy_key], wmax[copy_key]
+    f_scale = copy_fetch * 1024 / COPY_BYTES
+    w_scale = copy_write * 1024 / COPY_BYTES
 
     os.makedirs(a.out, exist_ok=True)
     kt = [f"# Kernel trace: {a.name}", "", "Command:", "", "```", a.command, "```", "",
@@ -111,8 +117,8 @@ def main():
 
     tr = [f"# HBM traffic: {a.name}", "", "Command:", "", "```", a.command, "```", "",
           f"Scale: the reference copy reads and writes {COPY_BYTES} bytes; per dispatch "
-          f"(grid {copy_key[1]}, {nf[copy_key]} dispatches) FETCH_SIZE reads "
-          f"{fetch[copy_key]:.1f} KiB and WRITE_SIZE {write[copy_key]:.1f} KiB, "
+          f"(grid {copy_key[1]}, the largest of its {nf[copy_key]} copy dispatches) FETCH_SIZE "
+          f"reads {copy_fetch:.1f} KiB and WRITE_SIZE {copy_write:.1f} KiB, "
           f"so bytes = FETCH_SIZE KiB * 1024 / {f_scale:.5f} and "
           f"WRITE_SIZE KiB * 1024 / {w_scale:.5f}.", "",
           "| kernel | grid (work-items) | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB "

@@ -21,7 +21,8 @@ Default run (prints ONE JSON line):
   o_proj sweep, the KDA sweep, the DSA sweep to B=256), each call on a
   distinct weight copy from a rotation of >= 1 GB (cold: no call finds its
   weight in the MALL): us per call back to back (one pair of events around
-  the calls) and by per-call event pairs (median), GB/s and % of 8 TB/s;
+  the calls) and by per-call event pairs (median, p10, p90), GB/s, % of 8 TB/s and %
+  of the box's sustained read rate (the 2 GB read of read_ceiling);
   TFLOP/s and % of the 2.5 PFLOP/s BF16 MFMA peak for B >= 64.
 * read_ceiling: the library's streaming-read probe over the chain's weights
   back to back and over a 2 GB buffer (the box's plain read rates).
@@ -341,8 +342,9 @@ def overlap_study(torch, wl, timing, stack, x0, y_in, y_o, reps):
     return out
 
 
-def per_config(args, torch, tp, wl, timing, report):
-    """Every batch point of the four single-projection workloads, cold."""
+def per_config(args, torch, tp, wl, timing, report, ceiling_gbps=None):
+    """Every batch point of the four single-projection workloads, cold; with
+    the box's sustained read rate (GB/s) known, also each point's share of it."""
     dev = torch.device("cuda:0")
     names = SWEEPS if args.configs is None else \
         tuple(n for n in args.configs.split(",") if n and n != "none")
@@ -366,11 +368,14 @@ def per_config(args, torch, tp, wl, timing, report):
             nbytes = wl.algorithmic_bytes(B, cfg.N, cfg.K)
             b2b = cold["us_mean_b2b"]
             p = {"us_b2b": round(b2b, 2), "us_median": round(cold["us_median"], 2),
+                 "us_p10": round(cold["us_p10"], 2), "us_p90": round(cold["us_p90"], 2),
                  "GBps_b2b": round(timing.gbs(nbytes, b2b), 1),
                  "pct_peak_b2b": round(100 * timing.gbs(nbytes, b2b) / timing.HBM_PEAK_GBS, 1),
                  "pct_peak_median": round(100 * timing.gbs(nbytes, cold["us_median"])
                                           / timing.HBM_PEAK_GBS, 1),
                  "kernel": plan.kernel_name(B)}
+            if ceiling_gbps:
+                p["pct_read_ceiling_b2b"] = round(100 * timing.gbs(nbytes, b2b) / ceiling_gbps, 1)
             if B >= 64:
                 tf = 2.0 * B * cfg.N * cfg.K / (b2b * 1e-6) / 1e12
                 p["TFLOPs_b2b"] = round(tf, 1)
@@ -532,7 +537,8 @@ def main():
     report = {} if args.report else None
     pc = None
     if not args.headline_only and args.configs != "none":
-        pc = per_config(args, torch, tp, wl, timing, report)
+        pc = per_config(args, torch, tp, wl, timing, report,
+                        ceiling_gbps=h["read_ceiling"]["sustained_2GB_GBps"])
     front = None
     if not args.headline_only and args.configs != "none":
         front = moe_front(args, torch, tp, wl, timing)

@@ -15,6 +15,15 @@ from __future__ import annotations
 from ._binding import Plan, pack_rows
 
 
+def _stream_object(stream):
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream()
+    if isinstance(stream, int):
+        return torch.cuda.ExternalStream(stream)
+    return stream
+
+
 class MoeFront:
     """A split-K front over BF16 weights [rows_i, K] that share the input x."""
 
@@ -24,6 +33,9 @@ class MoeFront:
         self.N = sum(self.rows)
         self.K = int(parts[0].shape[1])
         self.weight = pack_rows(parts, stream=stream)   # one [N, K] weight
+        # packing is a one-time preparation: wait for it here, so that a call
+        # on any stream reads the packed weight
+        _stream_object(stream).synchronize()
         self.plan = Plan(self.N, self.K, batches)
         self.front_max = max(batches)
 

@@ -38,6 +38,10 @@ Default run (prints ONE JSON line):
   cores, over a bounded number of layers; its CPU model; and a one-thread
   figure for the DSA B=1 workload.
 
+`--ring-probe` times only the projection kernel's LDS-ring loads without its
+arithmetic (proj_ring_probe): x alone, the weight alone, both, and variants of
+piece width, barrier and bytes in flight.
+
 `--report PATH` also writes every point's hot figure (one weight repeated,
 cache-assisted) and the graph-replayed chain to PATH as JSON.
 """
@@ -84,6 +88,9 @@ def _args():
     ap.add_argument("--front-no-separate", action="store_true",
                     help="skip the separate-launch comparison (a profile then holds only "
                          "front launches)")
+    ap.add_argument("--ring-probe", action="store_true",
+                    help="time only the LDS-ring load probe (the projection kernel's loads "
+                         "without its arithmetic) and print it as one JSON line")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="wall time of the bounded oracle sample (whole layers)")
@@ -448,6 +455,54 @@ def moe_front(args, torch, tp, wl, timing):
     return out
 
 
+# (label, stage rows, piece bytes, stages, barrier, what, shared weight)
+RING_CASES = (
+    ("x only", 64, 256, 5, 1, 1, 0),
+    ("weight only (a private block per workgroup: HBM)", 64, 256, 5, 1, 2, 0),
+    ("weight only (one block for all: L2 / MALL)", 64, 256, 5, 1, 2, 1),
+    ("x + private weight", 128, 256, 3, 1, 3, 0),
+    ("x + shared weight", 128, 256, 3, 1, 3, 1),
+    ("x only, no barrier", 64, 256, 5, 0, 1, 0),
+    ("x only, 512-byte pieces", 64, 512, 3, 1, 1, 0),
+    ("x only, 512-byte pieces, no barrier", 64, 512, 3, 0, 1, 0),
+    ("x only, 1 KB pieces", 64, 1024, 2, 1, 1, 0),
+    ("x only, 1 KB pieces, no barrier", 64, 1024, 2, 0, 1, 0),
+    ("x only, twice the bytes in flight", 64, 256, 9, 1, 1, 0),
+    ("x + private weight, twice the bytes in flight", 128, 256, 5, 1, 3, 0),
+)
+
+
+def ring_probe_study(torch, tp, timing):
+    """The pipelined kernel's LDS-ring loads alone (proj_ring_probe) over 256
+    workgroups, one per compute unit, each reading 917,504 bytes per 64
+    stage rows (64 rows x 7168 BF16): x, shared by every workgroup, and the
+    weight, a private block per workgroup (two copies alternated, 470 MB, so
+    it comes from HBM) or one block for all."""
+    dev = torch.device("cuda:0")
+    K, grid = 7168, 256
+    g = torch.Generator(device=dev)
+    g.manual_seed(77)
+    x = (torch.randn((64, K), generator=g, device=dev)).to(torch.bfloat16)
+    ws = [(torch.randn((grid * 64, K), generator=g, device=dev) * 0.02).to(torch.bfloat16)
+          for _ in range(2)]
+    sink = torch.empty(grid * 8, dtype=torch.float32, device=dev)
+    out = []
+    for label, rows, piece, depth, barrier, what, shared in RING_CASES:
+        calls = [(lambda w=w: tp.ring_probe(x, w, rows=rows, piece=piece, depth=depth,
+                                            barrier=bool(barrier), what=what,
+                                            shared_w=bool(shared), grid=grid, sink=sink))
+                 for w in ws]
+        r = timing.time_calls(calls, warmup=3, reps=40, warm_seconds=0.05)
+        per_cu = rows * K * 2
+        row = {"case": label, "rows": rows, "piece": piece, "stages": depth,
+               "inflight_KB": (depth - 1) * rows * piece // 1024, "barrier": bool(barrier),
+               "us_b2b": round(r["us_mean_b2b"], 2),
+               "GBps_per_CU": round(per_cu / r["us_mean_b2b"] / 1e3, 1)}
+        out.append(row)
+        _say(f"ring probe {label:48s} {row['us_b2b']:6.2f} us  {row['GBps_per_CU']:5.1f} GB/s per CU")
+    return {"K": K, "workgroups": grid, "bytes_per_64_rows": 64 * K * 2, "cases": out}
+
+
 def _cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -518,6 +573,9 @@ def main():
         print(json.dumps({"error": "no GPU visible"}))
         sys.exit(1)
     torch.cuda.set_device(0)
+    if args.ring_probe:
+        print(json.dumps({"ring_probe": ring_probe_study(torch, tp, timing)}), flush=True)
+        return
     if args.front_only:
         front = moe_front(args, torch, tp, wl, timing)
         if args.copy_calibration:

@@ -336,6 +336,28 @@ size_t proj_plan_workspace_bytes(const proj_plan_t *plan);
 int proj_read_probe(const void *buf, size_t bytes, float *sink,
                     int waves_per_cu, void *stream);
 
+/*
+ * proj_ring_probe -- measurement aid, not part of the projection: enqueue
+ * the loads of the pipelined MFMA kernel's LDS ring alone (eight waves per
+ * workgroup, a ring of `depth` stages of `rows` rows x `piece` bytes filled
+ * by direct-to-LDS 128-bit loads, one wait and, with `barrier`, one
+ * workgroup barrier per stage; no arithmetic), over `grid` workgroups, each
+ * walking the K * 2 / piece chunks of its rows once.
+ *   x       : BF16 [64, K] device buffer; with what & 1, stage rows 0..63
+ *             read it with cached loads (every workgroup the same rows)
+ *   w       : BF16 [grid * 64, K] device buffer (workgroup g reads rows
+ *             64g..64g+63 with non-temporal loads), or [64, K] with shared_w
+ *   what    : 1 = x rows only (rows 64), 2 = weight rows only (rows 64),
+ *             3 = x rows then weight rows (rows 128)
+ *   rows, piece, depth, barrier : one of the compiled combinations (64, 256,
+ *             5, 0/1), (128, 256, 3, 1), (64, 512, 3, 0/1), (64, 1024, 2,
+ *             0/1), (64, 256, 9, 1), (128, 256, 5, 1); K * 2 % piece == 0
+ *   sink    : device floats, grid * 8 of them (each wave writes one)
+ * Returns PROJ_OK, PROJ_EINVAL, PROJ_EALIGN or PROJ_EHIP.
+ */
+int proj_ring_probe(const void *x, const void *w, int K, int rows, int piece, int depth,
+                    int barrier, int what, int shared_w, int grid, float *sink, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

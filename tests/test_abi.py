@@ -377,3 +377,22 @@ def test_unmeasured_shape_takes_the_nearest_measured_tactic():
     assert far.tactic(64)[0].kernel == tp.KERNEL_MFMA_PIPE
     # the measured shapes themselves are unchanged
     assert ref.tactic(1)[0] != far.tactic(1)[0]
+
+
+def test_ring_probe_argument_checks_on_the_host():
+    # refused before any HIP call (the pointers are never used)
+    p, s = 0x100000, 0x800000
+    lib = tp.library()
+    def probe(*a):
+        import ctypes
+        x, w, K, rows, piece, depth, barrier, what, shared, grid, sink = a
+        return lib.proj_ring_probe(ctypes.c_void_p(x), ctypes.c_void_p(w), K, rows, piece,
+                                   depth, barrier, what, shared, grid, ctypes.c_void_p(sink),
+                                   ctypes.c_void_p(0))
+    assert probe(0, p, 7168, 64, 256, 5, 1, 1, 0, 4, s) == tp.PROJ_EINVAL       # no x
+    assert probe(p, p, 7168, 64, 256, 5, 1, 3, 0, 4, s) == tp.PROJ_EINVAL       # both needs 128 rows
+    assert probe(p, p, 7168, 128, 256, 3, 1, 1, 0, 4, s) == tp.PROJ_EINVAL      # 128 rows needs both
+    assert probe(p, p, 7168, 64, 256, 7, 1, 1, 0, 4, s) == tp.PROJ_EINVAL       # not compiled
+    assert probe(p, p, 7000, 64, 1024, 2, 1, 1, 0, 4, s) == tp.PROJ_EINVAL      # K*2 % piece
+    assert probe(p, p, 7168, 64, 256, 5, 1, 1, 0, 0, s) == tp.PROJ_EINVAL       # empty grid
+    assert probe(p + 8, p, 7168, 64, 256, 5, 1, 1, 0, 4, s) == tp.PROJ_EALIGN

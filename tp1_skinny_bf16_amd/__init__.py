@@ -13,6 +13,7 @@ from ._binding import (EXPORTS, KERNEL_IDS, KERNEL_NAMES,  # noqa: F401
                        LIB_PATH, MAX_BATCH, MAX_BATCHES, MAX_PACK, PROJ_EALIGN, PROJ_EBATCH,
                        PROJ_EHIP, PROJ_EINVAL, PROJ_ENODEV, PROJ_ENOMEM, PROJ_ESCRATCH,
                        PROJ_OK, Plan, ProjError, Tactic, library, pack_rows, pack_rows_ptr,
-                       prefetch, read_probe, run_noalloc, run_noalloc_ptr, strerror)
+                       prefetch, read_probe, ring_probe, run_noalloc, run_noalloc_ptr,
+                       strerror)
 from .front import MoeFront  # noqa: F401
 from .layers import LayerStack  # noqa: F401

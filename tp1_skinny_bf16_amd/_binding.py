@@ -42,7 +42,7 @@ EXPORTS = ("proj_plan", "proj_run", "proj_free", "proj_strerror",
            "proj_plan_tactic", "proj_plan_set_tactic",
            "proj_plan_workspace_bytes", "proj_read_probe", "proj_run_layers",
            "proj_plan_kernel_name", "proj_run_noalloc", "proj_prefetch",
-           "proj_run_layers_overlap", "proj_pack_rows")
+           "proj_run_layers_overlap", "proj_pack_rows", "proj_ring_probe")
 
 
 class ProjError(RuntimeError):
@@ -127,6 +127,9 @@ def _lib():
     lib.proj_pack_rows.argtypes = [vp, ctypes.POINTER(vp), ctypes.POINTER(ctypes.c_int),
                                    ctypes.c_int, ctypes.c_int, vp]
     lib.proj_pack_rows.restype = ctypes.c_int
+    ci = ctypes.c_int
+    lib.proj_ring_probe.argtypes = [vp, vp, ci, ci, ci, ci, ci, ci, ci, ci, vp, vp]
+    lib.proj_ring_probe.restype = ctypes.c_int
     lib.proj_run_layers_overlap.argtypes = [vp, vp, ctypes.c_int, ctypes.c_int, vp, ctypes.c_long,
                                             ctypes.POINTER(vp), ctypes.POINTER(vp), vp, vp,
                                             ctypes.c_double, ctypes.c_size_t, vp, vp]
@@ -345,6 +348,27 @@ def pack_rows(weights, out=None, stream=None):
     _check(pack_rows_ptr(out.data_ptr(), [w.data_ptr() for w in weights], rows, K,
                          _stream_handle(stream)), "proj_pack_rows")
     return out
+
+
+def ring_probe(x, w, *, rows: int, piece: int, depth: int, barrier: bool, what: int,
+               shared_w: bool, grid: int, sink, stream=None):
+    """Enqueue the LDS-ring load probe (measurement aid): x [64, K] and w
+    [grid * 64, K] (or [64, K] with shared_w) BF16 device tensors, sink a
+    float32 device tensor of at least grid * 8 elements."""
+    K = x.shape[1]
+    need_w = 64 if shared_w else grid * 64
+    if tuple(x.shape) != (64, K) or w.shape[1] != K or w.shape[0] < need_w:
+        raise ValueError("x must be [64, K] and w at least [grid * 64, K] (or [64, K] shared)")
+    if sink.numel() < grid * 8 or sink.dtype.itemsize != 4:
+        raise ValueError("sink needs grid * 8 float32 elements")
+    if not (x.is_contiguous() and w.is_contiguous() and sink.is_contiguous()):
+        raise ValueError("x, w and sink must be contiguous")
+    _same_device(x, w, sink)
+    rc = _lib().proj_ring_probe(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(w.data_ptr()), K,
+                                int(rows), int(piece), int(depth), int(bool(barrier)), int(what),
+                                int(bool(shared_w)), int(grid), ctypes.c_void_p(sink.data_ptr()),
+                                ctypes.c_void_p(_stream_handle(stream)))
+    _check(rc, "proj_ring_probe")
 
 
 def read_probe(buf, sink, waves_per_cu: int = 0, stream=None):

@@ -17,7 +17,7 @@ ROOT = os.path.dirname(PKG)
 LIB = os.path.join(PKG, "libtp1proj.so")
 ARCH = os.environ.get("TP1_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["plan.cpp", "tactics_table.cpp", "proj_abi.hip", "kernels.hip"]
+SOURCES = ["plan.cpp", "tactics_table.cpp", "proj_abi.hip", "kernels.hip", "probes.hip"]
 
 HIPCC_FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

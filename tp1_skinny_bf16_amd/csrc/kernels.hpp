@@ -57,4 +57,11 @@ hipError_t launch_core_prefetch(unsigned long long ticks, const void *buf, size_
 hipError_t launch_read_probe(const void *buf, size_t bytes, float *sink,
                              int waves_per_cu, int num_cus, hipStream_t stream);
 
+// The LDS-ring load probe (probes.hip): the compiled (rows, piece, depth,
+// barrier) combinations, and its launch over `grid` workgroups of 512 lanes.
+bool ring_probe_instance_exists(int rows, int piece, int depth, bool barrier);
+hipError_t launch_ring_probe(const void *x, const void *w, long pitch, int C, int rows, int piece,
+                             int depth, bool barrier, int what, int shared_w, int grid,
+                             float *sink, hipStream_t stream);
+
 }  // namespace tp1

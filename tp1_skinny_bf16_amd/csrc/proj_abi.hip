@@ -542,4 +542,22 @@ int proj_read_probe(const void *buf, size_t bytes, float *sink, int waves_per_cu
     return e == hipSuccess ? PROJ_OK : PROJ_EHIP;
 }
 
+int proj_ring_probe(const void *x, const void *w, int K, int rows, int piece, int depth,
+                    int barrier, int what, int shared_w, int grid, float *sink, void *stream) {
+    if (!x || !w || !sink || K <= 0 || grid < 1 || grid > 65536) return PROJ_EINVAL;
+    if (what < 1 || what > 3 || (what == 3) != (rows == 128)) return PROJ_EINVAL;
+    if (piece <= 0 || ((long)K * 2) % piece != 0) return PROJ_EINVAL;
+    if (!tp1::ring_probe_instance_exists(rows, piece, depth, barrier != 0)) return PROJ_EINVAL;
+    if (!aligned16(x) || !aligned16(w) || ((long)K * 2) % 16 != 0) return PROJ_EALIGN;
+    const int C = (int)((long)K * 2 / piece);
+    const hipError_t e =
+        tp1::launch_ring_probe(x, w, (long)K * 2, C, rows, piece, depth, barrier != 0, what,
+                               shared_w ? 1 : 0, grid, sink, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) {
+        (void)hipGetLastError();
+        return PROJ_EHIP;
+    }
+    return PROJ_OK;
+}
+
 }  // extern "C"

@@ -161,7 +161,9 @@ int proj_plan(int N, int K, const int *batches, int n_batches, unsigned flags,
  *   W      : BF16 [N, K] device pointer, contiguous rows, 16-byte aligned
  *   y      : BF16 [B, N] device pointer, contiguous (row stride N),
  *            16-byte aligned; must not overlap x or W
- *   stream : a hipStream_t (NULL = the default stream)
+ *   stream : a hipStream_t of the plan's device (NULL = the default stream)
+ * The current device must be the one the plan was built on (its workspace
+ * lives there): otherwise PROJ_EINVAL, before any launch.
  * One plan supports one stream at a time: runs on different streams that
  * overlap in time share the plan's workspace and race.
  * proj_run only launches kernels (one, or two with a split-K pass): no

@@ -184,6 +184,11 @@ class Plan:
         _check(rc, f"proj_plan(N={N}, K={K}, batches={self.batches})")
         self._h = h
         self.host_only = host_only
+        # the device the plan's workspace lives on (the current one now)
+        self.device = None
+        if not host_only:
+            import torch
+            self.device = torch.cuda.current_device()
 
     def close(self):
         h, self._h = getattr(self, "_h", None), None
@@ -258,6 +263,8 @@ class Plan:
                 out.dtype != torch.bfloat16:
             raise ValueError("out must be a contiguous bfloat16 [B, N] tensor")
         _same_device(x, W, out)
+        if self.device is not None and x.device.index != self.device:
+            raise ValueError(f"operands on cuda:{x.device.index}, the plan on cuda:{self.device}")
         ldx = x.stride(0) if B > 1 else self.K
         rc = self.run_ptr(B, x.data_ptr(), ldx, W.data_ptr(), out.data_ptr(),
                           _stream_handle(stream))

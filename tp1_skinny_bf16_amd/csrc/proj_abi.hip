@@ -295,6 +295,10 @@ int proj_run(const proj_plan_t *plan, int B, const void *x, long ldx, const void
     const uintptr_t we = wb + (uintptr_t)c.N * c.K * 2u;
     if ((yb < xe && xb < ye) || (yb < we && wb < ye)) return PROJ_EINVAL;
     if (c.flags & PROJ_PLAN_HOST_ONLY) return PROJ_ENODEV;
+    // the workspace (and any counters) live on the plan's device: launching
+    // on another would hand its kernels another GPU's memory
+    int cur = -1;
+    if (hipGetDevice(&cur) != hipSuccess || cur != plan->device) return PROJ_EINVAL;
     const int i = tp1::bin_index(c, B);
     if (i < 0) return PROJ_EBATCH;
     const proj_tactic_t &t = c.tactics[i];

@@ -25,6 +25,10 @@ class LayerStack:
         for w in list(w_in) + list(w_o):
             if not w.is_contiguous() or not w.is_cuda:
                 raise ValueError("weights must be contiguous device tensors")
+        weights = list(w_in) + list(w_o)
+        devs = {p.device for p in (in_plan, out_plan)} | {w.device.index for w in weights}
+        if len(devs) != 1:
+            raise ValueError("the plans and every weight must be on one device")
         self.in_plan, self.out_plan = in_plan, out_plan
         self.w_in, self.w_o = list(w_in), list(w_o)   # keep the tensors alive
         L = len(self.w_in)

@@ -469,6 +469,9 @@ RING_CASES = (
     ("x only, 1 KB pieces, no barrier", 64, 1024, 2, 0, 1, 0),
     ("x only, twice the bytes in flight", 64, 256, 9, 1, 1, 0),
     ("x + private weight, twice the bytes in flight", 128, 256, 5, 1, 3, 0),
+    ("x only, 128-byte pieces", 64, 128, 9, 1, 1, 0),
+    ("weight only (private), 128-byte pieces", 64, 128, 9, 1, 2, 0),
+    ("x + private weight, 128-byte pieces", 128, 128, 9, 1, 3, 0),
 )
 
 

@@ -353,7 +353,8 @@ int proj_read_probe(const void *buf, size_t bytes, float *sink,
  *             3 = x rows then weight rows (rows 128)
  *   rows, piece, depth, barrier : one of the compiled combinations (64, 256,
  *             5, 0/1), (128, 256, 3, 1), (64, 512, 3, 0/1), (64, 1024, 2,
- *             0/1), (64, 256, 9, 1), (128, 256, 5, 1); K * 2 % piece == 0
+ *             0/1), (64, 256, 9, 1), (128, 256, 5, 1), (64, 128, 9, 1),
+ *             (128, 128, 9, 1); K * 2 % piece == 0
  *   sink    : device floats, grid * 8 of them (each wave writes one)
  * Returns PROJ_OK, PROJ_EINVAL, PROJ_EALIGN or PROJ_EHIP.
  */

@@ -12,7 +12,7 @@ pytestmark = pytest.mark.gpu
 # (rows, piece, depth, barrier, what) for every compiled instance
 CASES = [(64, 256, 5, 1, 1), (64, 256, 5, 0, 2), (128, 256, 3, 1, 3), (64, 512, 3, 1, 1),
          (64, 512, 3, 0, 1), (64, 1024, 2, 1, 2), (64, 1024, 2, 0, 1), (64, 256, 9, 1, 1),
-         (128, 256, 5, 1, 3)]
+         (128, 256, 5, 1, 3), (64, 128, 9, 1, 2), (128, 128, 9, 1, 3)]
 
 
 @pytest.fixture(scope="module", autouse=True)

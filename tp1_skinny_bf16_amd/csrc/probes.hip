@@ -102,7 +102,7 @@ __global__ __launch_bounds__(512) void ring_probe_kernel(const char *x, const ch
 #define TP1_RING_PROBE_INSTANCES(X)                                                        \
     X(64, 256, 5, true) X(64, 256, 5, false) X(128, 256, 3, true) X(64, 512, 3, true)      \
     X(64, 512, 3, false) X(64, 1024, 2, true) X(64, 1024, 2, false) X(64, 256, 9, true)    \
-    X(128, 256, 5, true)
+    X(128, 256, 5, true) X(64, 128, 9, true) X(128, 128, 9, true)
 
 bool ring_probe_instance_exists(int rows, int piece, int depth, bool barrier) {
 #define TP1_RING_MATCH(R, P, DD, BB) \

@@ -396,3 +396,22 @@ def test_ring_probe_argument_checks_on_the_host():
     assert probe(p, p, 7000, 64, 1024, 2, 1, 1, 0, 4, s) == tp.PROJ_EINVAL      # K*2 % piece
     assert probe(p, p, 7168, 64, 256, 5, 1, 1, 0, 0, s) == tp.PROJ_EINVAL       # empty grid
     assert probe(p + 8, p, 7168, 64, 256, 5, 1, 1, 0, 4, s) == tp.PROJ_EALIGN
+
+
+def test_every_table_row_is_the_plans_choice():
+    # each measured row must pass the library's checks for its own shape and
+    # bin: a row that failed them would fall through to another rule unseen
+    import os
+    import re
+    src = open(os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))),
+                            "tp1_skinny_bf16_amd", "csrc", "tactics_table.cpp")).read()
+    names = {"PROJ_KERNEL_STREAM": tp.KERNEL_STREAM, "PROJ_KERNEL_STREAM_DOT2": tp.KERNEL_STREAM_DOT2,
+             "PROJ_KERNEL_MFMA_XS": tp.KERNEL_MFMA_XS, "PROJ_KERNEL_MFMA_PIPE": tp.KERNEL_MFMA_PIPE}
+    pat = r"\{(\d+), (\d+), (\d+), \{(PROJ_KERNEL_\w+), ([\d, ]+)\}\}"
+    rows = re.findall(pat, src)
+    assert len(rows) > 100
+    for N, K, b, kern, fields in rows:
+        vals = [int(v) for v in fields.split(",")]
+        want = tp.Tactic(names[kern], *vals)
+        plan = tp.Plan(int(N), int(K), [int(b)], host_only=True)
+        assert plan.tactic(int(b))[0] == want, (N, K, b)

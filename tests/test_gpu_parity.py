@@ -279,6 +279,32 @@ def test_multilayer_stream_per_layer_parity():
     say(f"final |y| rms = {float(y_o[-1].float().pow(2).mean().sqrt()):.4g}")
 
 
+@pytest.mark.parametrize("B", [37, 5])
+def test_layer_chain_ragged_batch(B):
+    """The chain at a batch inside a bin (B rows of a 16- or 64-row tile): the
+    padded rows of every tile, the gather through the in-projection's row
+    stride and the split-K passes at B < bin, per layer on the GPU's own
+    layer input."""
+    L = 2
+    g = torch.Generator().manual_seed(90 + B)
+    w_in = [wl.normal_bf16((wl.DSA_N, wl.DSA_K), wl.W_STD, g) for _ in range(L)]
+    w_o = [wl.normal_bf16((wl.OPROJ_N, wl.OPROJ_K), wl.W_STD, g) for _ in range(L)]
+    x0 = wl.normal_bf16((B, wl.DSA_K), wl.X_STD, g)
+    pin = tp.Plan(wl.DSA_N, wl.DSA_K, [16, 64])
+    po = tp.Plan(wl.OPROJ_N, wl.OPROJ_K, [16, 64])
+    say(f"chain B={B}: {pin.kernel_name(B)} / {po.kernel_name(B)}")
+    stack = tp.LayerStack(pin, po, [w.to(DEV) for w in w_in], [w.to(DEV) for w in w_o])
+    y_in, y_o = stack.run(x0.to(DEV))
+    torch.cuda.synchronize()
+    y_in, y_o = y_in.cpu(), y_o.cpu()
+    x_l = x0
+    for l in range(L):
+        check_random(f"chain B={B} layer {l} in-proj", wl.bits(y_in[l]), x_l, w_in[l])
+        check_random(f"chain B={B} layer {l} o_proj", wl.bits(y_o[l]),
+                     y_in[l][:, :wl.OPROJ_K], w_o[l])
+        x_l = y_o[l]
+
+
 def test_fused_split_matches_two_pass_bitwise():
     """The in-kernel split-K reduction (last workgroup to arrive sums the
     slices) and the two-pass reduction add the slices in the same order, so

@@ -17,6 +17,8 @@ Default run (prints ONE JSON line):
                 its average launch time, both measured live here with HIP
                 events on the launch stream, against the 8 TB/s HBM peak
     kernels   = both projections' average launch time and rate
+    layer_us  = each layer's time (its two calls) in the chain, median over
+                passes with an event between layers
 * per_config: every batch point of the other four workloads (DSA B=1, the
   o_proj sweep, the KDA sweep, the DSA sweep to B=256), each call on a
   distinct weight copy from a rotation of >= 1 GB (cold: no call finds its
@@ -227,6 +229,21 @@ def headline(args, torch, tp, wl, timing):
                      "GBps": round(timing.gbs(nbytes, us), 1),
                      "pct_peak": round(100 * timing.gbs(nbytes, us) / timing.HBM_PEAK_GBS, 1),
                      "TFLOPs": round(2.0 * B * N * K / (us * 1e-6) / 1e12, 1)}
+    # Each layer of the chain: the step's calls in order, an event after each
+    # layer, median over `steps` passes (a separate pass: the events between
+    # layers are not in the timed region above).
+    per_layer = [[] for _ in range(L)]
+    for _ in range(max(3, args.steps // 5)):
+        ev = _events(torch, L + 1)
+        ev[0].record(stream)
+        for l in range(L):
+            run_in(l)
+            run_o(l)
+            ev[l + 1].record(stream)
+        torch.cuda.synchronize()
+        for l in range(L):
+            per_layer[l].append(ev[l].elapsed_time(ev[l + 1]) * 1e3)
+    layer_us = [round(sorted(v)[len(v) // 2], 2) for v in per_layer]
     # restore the chain's outputs (the per-family passes rewrote them in place
     # with the same values, in the same order, so this is only for clarity)
     step()
@@ -260,7 +277,7 @@ def headline(args, torch, tp, wl, timing):
     graph = None
     if args.report:
         graph = timing.time_graph([step], replays=10)
-    return {"cfg": cfg, "t": t, "value": value, "ms": ms_per_step,
+    return {"cfg": cfg, "t": t, "value": value, "ms": ms_per_step, "layer_us": layer_us,
             "gpu_ms": gpu_ms_per_step, "step_bytes": step_bytes, "families": fam,
             "roofline": roof, "read_ceiling": ceiling, "graph_us": graph, "overlap": overlap,
             "stack": stack, "tensors": (w_in, w_o, x0, y_in, y_o)}
@@ -634,6 +651,7 @@ def main():
                    "layers": cfg.layers, "B": cfg.bmax, "step_bytes": h["step_bytes"],
                    "calls_per_step": 2 * cfg.layers},
         "kernels": h["families"],
+        "layer_us": h["layer_us"],
         "roofline": h["roofline"],
         "read_ceiling": h["read_ceiling"],
         "prefetch_overlap": h["overlap"],

@@ -37,8 +37,9 @@ Default run (prints ONE JSON line):
   projections, cold, at K = 7168 and B = 1..64; the pages print neither
   part's size, so the parts sweep 2048+1024, 4096+2048 and 8192+4096 rows.
 * cpu_baseline: the CPU oracle (FP64 sums) on the same chain, on all host
-  cores, over a bounded number of layers; its CPU model; and a one-thread
-  figure for the DSA B=1 workload.
+  cores, over a bounded number of layers; its CPU model; a one-thread
+  figure for the DSA B=1 workload; and one call of each single-projection
+  workload at its largest batch.
 
 `--ring-probe` times only the projection kernel's LDS-ring loads without its
 arithmetic (proj_ring_probe): x alone, the weight alone, both, and variants of
@@ -536,7 +537,8 @@ def _cpu_model() -> str:
 
 def cpu_baseline(args, h, wl):
     """The oracle on the multi-layer stream, layer by layer, chained on its
-    own outputs, until cpu_seconds have passed; and one thread on DSA B=1."""
+    own outputs, until cpu_seconds have passed; one thread on DSA B=1; and one
+    call of every single-projection workload at its largest batch."""
     import oracle
     cfg, t = h["cfg"], h["t"]
     threads = oracle.default_threads()
@@ -565,6 +567,19 @@ def cpu_baseline(args, h, wl):
     oracle.proj(x1, w1, threads=1)
     e1 = time.perf_counter() - t1
     n1 = wl.algorithmic_bytes(1, wl.DSA_N, wl.DSA_K)
+    # every single-projection workload: one call at its largest batch, all threads
+    per_cfg = {}
+    for name in SWEEPS:
+        c = wl.BY_NAME[name]
+        ct = wl.config_tensors(c)
+        xb_c, wb_c = wl.bits(ct["x"]), wl.bits(ct["W"])
+        B = c.bmax
+        tc = time.perf_counter()
+        oracle.proj(xb_c[:B], wb_c, threads=threads)
+        ec = time.perf_counter() - tc
+        per_cfg[name] = {"B": B, "ms_per_call": round(ec * 1e3, 1),
+                         "GBps": round(wl.algorithmic_bytes(B, c.N, c.K) / ec / 1e9, 3)}
+        del ct, xb_c, wb_c
     return {"value": round(nbytes / el / 1e9, 3), "unit": "GB/s", "cores": threads,
             "kind": "oracle", "cpu_model": _cpu_model(),
             "sample": f"{done} layers (in-projection then o_proj, B=64) of the 8-layer "
@@ -573,7 +588,8 @@ def cpu_baseline(args, h, wl):
             "ms_per_layer": round(el * 1e3 / done, 1),
             "ms_per_step_extrapolated": round(el * 1e3 / done * cfg.layers, 1),
             "t1_dsa_b1": {"threads": 1, "ms_per_call": round(e1 * 1e3, 1),
-                          "GBps": round(n1 / e1 / 1e9, 3)}}
+                          "GBps": round(n1 / e1 / 1e9, 3)},
+            "per_config": per_cfg}
 
 
 def main():

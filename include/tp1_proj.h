@@ -189,7 +189,9 @@ int proj_run(const proj_plan_t *plan, int B, const void *x, long ldx,
  * fixed gather of the first K_o columns, read in place through the row
  * stride N_in, without a copy).
  *   in, out : plans with out.N == in.K and out.K <= in.N; B must be within
- *             both plans' batch ranges
+ *             both plans' batch ranges; in.N % 8 == 0, since o_proj reads
+ *             each layer's input projection in place with row stride in.N
+ *             (else PROJ_EALIGN, before any launch)
  *   x0      : BF16 [B, K_in], row stride ldx0 (0 = K_in)
  *   W_in    : host array of L device pointers to BF16 [N_in, K_in]
  *   W_o     : host array of L device pointers to BF16 [N_o, K_o]

@@ -183,6 +183,13 @@ def test_run_layers_argument_checks():
     assert call(po, pin, 2, 64) == tp.PROJ_EINVAL        # wrong chain order
     assert call(pin, po, 2, 64, Wz) == tp.PROJ_EINVAL    # a NULL weight
     assert call(pin, po, -1, 64) == tp.PROJ_EINVAL
+    # an input projection of 1820 rows cannot feed o_proj in place (rows of
+    # 3640 bytes are not 16-byte aligned): refused before any launch
+    shard_in = tp.Plan(1820, 7168, [64], host_only=True)
+    shard_o = tp.Plan(7168, 1536, [64], host_only=True)
+    assert call(shard_in, shard_o, 2, 64) == tp.PROJ_EALIGN
+    assert lib.proj_run_layers(pin.handle, po.handle, 2, 64, ctypes.c_void_p(X + 8), 0, W, W,
+                               ctypes.c_void_p(Y1), ctypes.c_void_p(Y2), None) == tp.PROJ_EALIGN
 
 
 def test_run_layers_overlap_argument_checks():

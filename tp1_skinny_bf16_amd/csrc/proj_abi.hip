@@ -124,6 +124,19 @@ int noalloc_device(int dev, NoallocDevice **out) {
     return PROJ_OK;
 }
 
+// The layer chain's alignment, checked before its first launch: o_proj reads
+// each layer's input projection in place through row stride N_in, so N_in
+// must keep rows 16-byte aligned (then every layer's slice of y_in and y_o,
+// B*N_in and B*K_in elements apart, starts aligned too); and the first
+// layer's operands must be aligned as proj_run requires.
+int chain_alignment(const tp1::PlanCore &in, const void *x0, long ldx0, const void *y_in,
+                    const void *y_o) {
+    if ((in.N % 8) != 0) return PROJ_EALIGN;
+    if (!aligned16(x0) || !aligned16(y_in) || !aligned16(y_o)) return PROJ_EALIGN;
+    if ((ldx0 % 8) != 0) return PROJ_EALIGN;
+    return PROJ_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -330,6 +343,8 @@ int proj_run_layers(const proj_plan_t *in, const proj_plan_t *out, int L, int B,
     if (!x0 || !y_in || !y_o) return PROJ_EINVAL;
     for (int l = 0; l < L; ++l)
         if (!W_in[l] || !W_o[l]) return PROJ_EINVAL;
+    const int al = chain_alignment(a, x0, ldx0, y_in, y_o);
+    if (al != PROJ_OK) return al;
     const size_t in_stride = (size_t)B * a.N * 2u;   // bytes per layer
     const size_t o_stride = (size_t)B * b.N * 2u;
     const void *x = x0;
@@ -381,6 +396,8 @@ int proj_run_layers_overlap(const proj_plan_t *in, const proj_plan_t *out, int L
     if (!x0 || !y_in || !y_o) return PROJ_EINVAL;
     for (int l = 0; l < L; ++l)
         if (!W_in[l] || !W_o[l]) return PROJ_EINVAL;
+    const int al = chain_alignment(a, x0, ldx0, y_in, y_o);
+    if (al != PROJ_OK) return al;
     if (a.flags & PROJ_PLAN_HOST_ONLY || b.flags & PROJ_PLAN_HOST_ONLY) return PROJ_ENODEV;
     int rate_khz = 0, cus = 0;
     if (hipDeviceGetAttribute(&rate_khz, hipDeviceAttributeWallClockRate, in->device) !=

@@ -29,6 +29,8 @@ class MoeFront:
 
     def __init__(self, parts, batches, *, stream=None):
         parts = list(parts)
+        if not parts:
+            raise ValueError("a front needs at least one weight")
         self.rows = [int(p.shape[0]) for p in parts]
         self.N = sum(self.rows)
         self.K = int(parts[0].shape[1])
